@@ -1,0 +1,55 @@
+"""Planted mistakes in copies of the CPU oracle must each fail at least one pin.
+
+Every mutant is a plausible slip (a transposed operand, a dropped term, a wrong
+sign, an off-by-one exponent bias, a wrong padding sign, swapped filter taps, a
+missing absolute value).  The mutated source is compiled on the CPU into a
+temporary directory; the real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle.build import SRC, build
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "transposed_A_index": ("Ad[i * K + k] = dec(a_col_major ? A[k * lda + i] : A[i * lda + k], dtype);",
+                           "Ad[i * K + k] = dec(a_col_major ? A[i * lda + k] : A[k * lda + i], dtype);"),
+    "dropped_last_k": ("for (int64_t k = 0; k < K; k++) { /* i-k-j",
+                       "for (int64_t k = 0; k + 1 < K; k++) { /* i-k-j"),
+    "wrong_sign": ("                c[j] += prod;", "                c[j] -= prod;"),
+    "bf16_shift": ("((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    "fp16_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    "fp16_subnormal_scale": ("ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    "conv_pad_sign": ("const int64_t h = p * jb->sh - jb->ph + r * jb->dh;",
+                      "const int64_t h = p * jb->sh + jb->ph + r * jb->dh - 2 * jb->ph * (p > 0);"),
+    "conv_swapped_rs": ("const uint16_t *wp = jb->w + ((k * jb->R + r) * jb->S + s) * jb->C;",
+                        "const uint16_t *wp = jb->w + ((k * jb->R + (jb->R - 1 - r)) * jb->S + s) * jb->C;"),
+    "sample_no_abs": ("            sacc += fabs(a * b);", "            sacc += a * b;"),
+    "sample_B_transposed": ("jb->b_col_major ? jb->B[j * jb->ldb + k] : jb->B[k * jb->ldb + j]",
+                            "jb->b_col_major ? jb->B[k * jb->ldb + j] : jb->B[j * jb->ldb + k]"),
+    "conv_dilation_ignored": ("const int64_t w = q * jb->sw - jb->pw + s * jb->dw;",
+                              "const int64_t w = q * jb->sw - jb->pw + s;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation target for {name} not found exactly once"
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = build(out=str(tmp_path / "libmutant.so"), src=str(msrc))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            ok, _ = pin(orc)
+        except Exception:  # a mutant may also make an entry point reject or crash-free misbehave
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
+    os.remove(lib)
