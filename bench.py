@@ -1,0 +1,208 @@
+"""Benchmark: TFLOP/s and fraction of MI355X dense bf16 MFMA peak on the 8192^3
+bf16 GEMM plus the 3x3 NHWC implicit-GEMM convolution.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  gemm_bf16  M = N = K = 8192, A and B row-major, U[-1, 1], bf16 output, and
+  conv2d_nhwc_implicit_gemm  N=32 H=W=56 C=K=256 3x3 s1 p1, x ~ N(0,1), w ~ N(0, 0.02), bf16 output.
+Inputs are resident in HBM before timing starts.  Both kernels run on torch's
+current HIP stream; HIP events on that stream bracket every launch.
+
+Prints ONE JSON line on stdout (details on stderr).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import implicit_gemm_conv_amd as igc  # noqa: E402
+from implicit_gemm_conv_amd import inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 flop/clk/CU x 2.4 GHz
+GEMM = "gemm_bf16_8192x8192x8192"
+CONV = "conv_bf16_n32_56x56_c256_k256_3x3"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(c):
+    return 2.0 * c["M"] * c["N"] * c["K"]
+
+
+def conv_geometry(c):
+    P = (c["H"] + 2 * c["ph"] - c["dh"] * (c["R"] - 1) - 1) // c["sh"] + 1
+    Q = (c["W"] + 2 * c["pw"] - c["dw"] * (c["S"] - 1) - 1) // c["sw"] + 1
+    return P, Q
+
+
+def conv_flops(c):
+    P, Q = conv_geometry(c)
+    return 2.0 * c["N"] * P * Q * c["K"] * c["R"] * c["S"] * c["C"]
+
+
+def cpu_baseline(gcfg, ccfg, A, B, x, w):
+    """The CPU oracle, as it is, on a bounded slice of the same step: the first rows of the GEMM output and the
+    first image of the convolution; the step time is extrapolated linearly in output elements."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    M, N, K = gcfg["M"], gcfg["N"], gcfg["K"]
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm(rows, N, K, A[:rows], K, oracle.ROW_MAJOR, B, N, oracle.ROW_MAJOR, oracle.BF16, threads=threads)
+    t_probe = time.perf_counter() - t0
+    # grow the slice to roughly 10 s of oracle work
+    rows = int(min(M, max(rows, rows * 10.0 / max(t_probe, 1e-3))))
+    rows = max(threads, rows // threads * threads)
+    t0 = time.perf_counter()
+    oracle.gemm(rows, N, K, A[:rows], K, oracle.ROW_MAJOR, B, N, oracle.ROW_MAJOR, oracle.BF16, threads=threads)
+    t_gemm = time.perf_counter() - t0
+    used = oracle.last_threads()
+    c = ccfg
+    n_img = 1
+    t0 = time.perf_counter()
+    oracle.conv2d_nhwc(n_img, c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], x[:n_img], w, oracle.BF16,
+                       c["sh"], c["sw"], c["ph"], c["pw"], c["dh"], c["dw"], threads=threads)
+    t_conv = time.perf_counter() - t0
+    step_s = t_gemm * (M / rows) + t_conv * (c["N"] / n_img)
+    value = (gemm_flops(gcfg) + conv_flops(ccfg)) / step_s / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"fp64 oracle on GEMM output rows 0..{rows - 1} (of {M}) in {t_gemm:.1f} s and conv image 0 "
+                      f"(of {c['N']}) in {t_conv:.1f} s, extrapolated per output element to one step "
+                      f"({step_s:.0f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune", type=str, default=None, help="bm,bn,bk,depth for the GEMM (default: built-in)")
+    ap.add_argument("--conv-tune", type=str, default=None, help="bm,bn,bk,depth for the conv (default: built-in)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    igc.lib()  # the HIP library must be built: no fallback
+    gtune = tuple(int(v) for v in args.tune.split(",")) if args.tune else None
+    ctune = tuple(int(v) for v in args.conv_tune.split(",")) if args.conv_tune else None
+
+    g = inputs.WORKLOADS[GEMM]
+    c = inputs.WORKLOADS[CONV]
+    log("generating inputs ...")
+    A, lda, B, ldb = inputs.workload_operands(GEMM)
+    x, w = inputs.workload_operands(CONV)
+    P, Q = conv_geometry(c)
+    dA = torch.from_numpy(A.view(np.int16)).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).cuda()
+    dC = torch.empty((g["M"], g["N"]), dtype=torch.bfloat16, device="cuda")
+    dx = torch.from_numpy(x.view(np.int16)).cuda()
+    dw = torch.from_numpy(w.view(np.int16)).cuda()
+    dy = torch.empty((c["N"] * P * Q * c["K"],), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        igc.check(igc.gemm_bf16_ex(g["M"], g["N"], g["K"], dA, lda, igc.ROW_MAJOR, dB, ldb, igc.ROW_MAJOR, dC,
+                                   g["N"], igc.OUT_BF16, gtune, stream))
+        if ev:
+            ev[1].record(stream)
+        igc.check(igc.conv2d_nhwc_implicit_gemm_ex(c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"],
+                                                   c["sw"], c["ph"], c["pw"], c["dh"], c["dw"], dx, dw, dy,
+                                                   igc.OUT_BF16, 0, ctune, stream))
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # spot check a few outputs against the oracle (untimed)
+    import oracle
+    from oracle import tolerance
+    rng = np.random.default_rng(0)
+    rows, cols = rng.integers(0, g["M"], 64), rng.integers(0, g["N"], 64)
+    ref, S = oracle.gemm_sample(g["M"], g["N"], g["K"], A, lda, 0, B, ldb, 0, oracle.BF16, rows, cols)
+    got = dC.float().cpu().numpy()[rows, cols]
+    ok_g = tolerance.check(got, ref, S, "bf16")[0]
+    idx = rng.integers(0, dy.numel(), 64)
+    yref, yS = oracle.conv2d_nhwc_sample(c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], x, w, oracle.BF16,
+                                         idx, c["sh"], c["sw"], c["ph"], c["pw"], c["dh"], c["dw"])
+    ok_c = tolerance.check(dy.float().cpu().numpy()[idx], yref, yS, "bf16")[0]
+    if not (ok_g and ok_c):
+        log(f"SELF-CHECK FAILED: gemm {ok_g} conv {ok_c}")
+        sys.exit(1)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gemm_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    conv_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    total_ms = evs[0][0].elapsed_time(evs[-1][2])
+    ms_per_step = total_ms / args.steps
+    gf, cf = gemm_flops(g), conv_flops(c)
+    value = (gf + cf) / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = gf / (gemm_ms.mean() * 1e-3) / 1e12
+    conv_tflops = cf / (conv_ms.mean() * 1e-3) / 1e12
+    log(f"gemm {gemm_ms.mean() * 1e3:.1f} us (median {np.median(gemm_ms) * 1e3:.1f}) = {gemm_tflops:.1f} TFLOP/s "
+        f"({100 * gemm_tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
+    log(f"conv {conv_ms.mean() * 1e3:.1f} us (median {np.median(conv_ms) * 1e3:.1f}) = {conv_tflops:.1f} TFLOP/s "
+        f"({100 * conv_tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
+    log(f"step {ms_per_step * 1e3:.1f} us -> {value:.1f} TFLOP/s; host wall {wall / args.steps * 1e3:.3f} ms/step")
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        base = cpu_baseline(g, c, A, B, x, w)
+        log(f"cpu baseline: {base}")
+
+    out = {
+        "metric": "TFLOP/s and % of bf16 MFMA peak, 8192^3 GEMM + 3x3 NHWC conv",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{GEMM} + {CONV}", "gemm": "M=N=K=8192 A,B row-major bf16 out",
+                   "conv": "N=32 H=W=56 C=K=256 R=S=3 stride 1 pad 1 NHWC/KRSC bf16 out",
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernels": {"gemm_us": round(float(gemm_ms.mean() * 1e3), 2), "gemm_tflops": round(gemm_tflops, 1),
+                    "conv_us": round(float(conv_ms.mean() * 1e3), 2), "conv_tflops": round(conv_tflops, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel (8192^3 bf16)"},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

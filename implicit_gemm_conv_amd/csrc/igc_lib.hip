@@ -1,0 +1,284 @@
+// igc_lib.hip -- C ABI of libigc: argument checks, instance selection, launch.
+//
+// Every entry point validates its arguments completely before it enqueues
+// anything, then launches one kernel on the caller's stream and returns.  The
+// library allocates nothing and keeps no state between calls.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/igc.h"
+#include "instances.hpp"
+#include "mainloop.hpp"
+#include "ring.hpp"
+
+namespace igc {
+
+static bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+static int out_size(igc_out_t t) { return t == IGC_OUT_F32 ? 4 : 2; }
+
+static const Instance* pick(const igc_tune_t* tune, bool fp16, bool a_kc, bool b_kc, bool conv, int64_t M,
+                            int64_t N, int64_t K) {
+    igc_tune_t t;
+    if (tune) {
+        t = *tune;
+    } else {
+        t = default_tune(M, N, K, conv);
+    }
+    return find_instance(t.bm, t.bn, t.bk, t.pipe_depth, fp16, a_kc, b_kc, conv);
+}
+
+static igc_status_t launch(const Instance* inst, const Params& p, hipStream_t stream) {
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    if (grid <= 0) return IGC_OK;
+    if (grid > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+    (void)hipGetLastError();  // launch errors below are ours alone
+    Params arg = p;
+    void* args[] = {&arg};
+    if (hipLaunchKernel(inst->fn, dim3((unsigned)grid), dim3(kThreads), args, 0, stream) != hipSuccess)
+        return IGC_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? IGC_OK : IGC_ERR_HIP;
+}
+
+static igc_status_t gemm_any(bool fp16, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             igc_layout_t la, const void* B, int64_t ldb, igc_layout_t lb, void* C, int64_t ldc,
+                             igc_out_t ct, const igc_tune_t* tune, hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0) return IGC_ERR_INVALID_VALUE;
+    if ((la != IGC_ROW_MAJOR && la != IGC_COL_MAJOR) || (lb != IGC_ROW_MAJOR && lb != IGC_COL_MAJOR))
+        return IGC_ERR_INVALID_VALUE;
+    if (ct != IGC_OUT_F32 && ct != IGC_OUT_BF16 && ct != IGC_OUT_F16) return IGC_ERR_INVALID_VALUE;
+    const bool a_kc = la == IGC_ROW_MAJOR, b_kc = lb == IGC_COL_MAJOR;
+    const Instance* inst = pick(tune, fp16, a_kc, b_kc, false, M, N, K);
+    if (!inst) return IGC_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return IGC_OK;
+    if (!C || ldc < N) return IGC_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (!A || !B) return IGC_ERR_INVALID_VALUE;
+        if (lda < (a_kc ? K : M) || ldb < (b_kc ? K : N)) return IGC_ERR_INVALID_VALUE;
+        if (!aligned16(A) || !aligned16(B) || (lda * 2) % 16 != 0 || (ldb * 2) % 16 != 0)
+            return IGC_ERR_MISALIGNED;
+        // Per-tile buffer offsets are 32-bit: one tile's rows must span < 2^31 bytes.
+        if (a_kc && (inst->bm * lda + inst->bk) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
+        if (b_kc && (inst->bn * ldb + inst->bk) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
+        if (!a_kc && (inst->bk * lda + inst->bm) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
+        if (!b_kc && (inst->bk * ldb + inst->bn) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(C) || (ldc * out_size(ct)) % 16 != 0) return IGC_ERR_MISALIGNED;
+
+    Params p = {};
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.tiles_m = (int)((M + inst->bm - 1) / inst->bm);
+    p.tiles_n = (int)((N + inst->bn - 1) / inst->bn);
+    if ((M + inst->bm - 1) / inst->bm > 0x7fffffff || (N + inst->bn - 1) / inst->bn > 0x7fffffff)
+        return IGC_ERR_UNSUPPORTED;
+    p.out_kind = (int)ct;
+    p.k_ragged8 = (K % 8) != 0;
+    p.vec_ok = 1;
+    return launch(inst, p, stream);
+}
+
+static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R, int S, int sh, int sw, int ph,
+                             int pw, int dh, int dw, const void* x, const void* w, void* y, igc_out_t yt,
+                             const igc_tune_t* tune, hipStream_t stream) {
+    if (N < 0 || K < 0 || H < 1 || W < 1 || C < 1 || R < 1 || S < 1 || sh < 1 || sw < 1 || ph < 0 || pw < 0 ||
+        dh < 1 || dw < 1)
+        return IGC_ERR_INVALID_VALUE;
+    if (yt != IGC_OUT_F32 && yt != IGC_OUT_BF16 && yt != IGC_OUT_F16) return IGC_ERR_INVALID_VALUE;
+    const int64_t hspan = (int64_t)H + 2LL * ph - (int64_t)dh * (R - 1) - 1;
+    const int64_t wspan = (int64_t)W + 2LL * pw - (int64_t)dw * (S - 1) - 1;
+    if (hspan < 0 || wspan < 0) return IGC_ERR_INVALID_VALUE;
+    const int64_t P = hspan / sh + 1, Q = wspan / sw + 1;
+    const int64_t Mg = (int64_t)N * P * Q, Ng = K, Kg = (int64_t)R * S * C;
+    const Instance* inst = pick(tune, fp16, true, true, true, Mg, Ng, Kg);
+    if (!inst) return IGC_ERR_UNSUPPORTED;
+    if (Mg == 0 || Ng == 0) return IGC_OK;
+    if (!x || !w || !y) return IGC_ERR_INVALID_VALUE;
+    if (C % 8 != 0) return IGC_ERR_MISALIGNED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return IGC_ERR_MISALIGNED;
+    if ((int64_t)N * H * W * C * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
+    if ((inst->bn * Kg + inst->bk) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
+    if (P > 0x7fff || Q > 0x7fff || Kg > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+
+    Params p = {};
+    p.A = x;
+    p.B = w;
+    p.C = y;
+    p.M = Mg;
+    p.N = Ng;
+    p.K = Kg;
+    p.lda = 0;
+    p.ldb = Kg;
+    p.ldc = K;
+    p.tiles_m = (int)((Mg + inst->bm - 1) / inst->bm);
+    p.tiles_n = (int)((Ng + inst->bn - 1) / inst->bn);
+    if ((Mg + inst->bm - 1) / inst->bm > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+    p.out_kind = (int)yt;
+    p.k_ragged8 = 0;  // C % 8 == 0
+    p.vec_ok = (K % 8) == 0;  // NPQK rows are K elements: vector stores need 16-byte rows
+    p.H = H;
+    p.W = W;
+    p.Cin = C;
+    p.R = R;
+    p.S = S;
+    p.P = (int)P;
+    p.Q = (int)Q;
+    p.sh = sh;
+    p.sw = sw;
+    p.ph = ph;
+    p.pw = pw;
+    p.dh = dh;
+    p.dw = dw;
+    return launch(inst, p, stream);
+}
+
+}  // namespace igc
+
+using namespace igc;
+
+extern "C" {
+
+igc_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, igc_layout_t la, const void* B,
+                       int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type, igc_stream_t stream) {
+    return gemm_any(false, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, nullptr, (hipStream_t)stream);
+}
+
+igc_status_t gemm_fp16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, igc_layout_t la, const void* B,
+                       int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type, igc_stream_t stream) {
+    return gemm_any(true, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, nullptr, (hipStream_t)stream);
+}
+
+igc_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, igc_layout_t la,
+                          const void* B, int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type,
+                          const igc_tune_t* tune, igc_stream_t stream) {
+    return gemm_any(false, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, tune, (hipStream_t)stream);
+}
+
+igc_status_t gemm_fp16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, igc_layout_t la,
+                          const void* B, int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type,
+                          const igc_tune_t* tune, igc_stream_t stream) {
+    return gemm_any(true, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, tune, (hipStream_t)stream);
+}
+
+igc_status_t conv2d_nhwc_implicit_gemm(int N, int H, int W, int C, int K, int R, int S, int stride_h, int stride_w,
+                                       int pad_h, int pad_w, int dil_h, int dil_w, const void* x, const void* w,
+                                       void* y, igc_out_t y_type, igc_stream_t stream) {
+    return conv_any(false, N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, w, y, y_type,
+                    nullptr, (hipStream_t)stream);
+}
+
+igc_status_t conv2d_nhwc_implicit_gemm_fp16(int N, int H, int W, int C, int K, int R, int S, int stride_h,
+                                            int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                            const void* x, const void* w, void* y, igc_out_t y_type,
+                                            igc_stream_t stream) {
+    return conv_any(true, N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, w, y, y_type,
+                    nullptr, (hipStream_t)stream);
+}
+
+igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int R, int S, int stride_h,
+                                          int stride_w, int pad_h, int pad_w, int dil_h, int dil_w, const void* x,
+                                          const void* w, void* y, igc_out_t y_type, int fp16,
+                                          const igc_tune_t* tune, igc_stream_t stream) {
+    return conv_any(fp16 != 0, N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, w, y,
+                    y_type, tune, (hipStream_t)stream);
+}
+
+int igc_tune_supported(const igc_tune_t* tune) {
+    if (!tune) return 0;
+    return find_instance(tune->bm, tune->bn, tune->bk, tune->pipe_depth, false, true, false, false) != nullptr;
+}
+
+int igc_tune_count(void) { return num_tunes(); }
+
+int igc_tune_get(int i, igc_tune_t* out) {
+    if (!out || i < 0 || i >= num_tunes()) return 0;
+    *out = tune_at(i);
+    return 1;
+}
+
+int64_t igc_tune_lds_bytes(const igc_tune_t* tune) {
+    if (!tune) return 0;
+    const Instance* inst = find_instance(tune->bm, tune->bn, tune->bk, tune->pipe_depth, false, true, false, false);
+    return inst ? inst->lds_bytes : 0;
+}
+
+const char* igc_status_string(igc_status_t status) {
+    switch (status) {
+        case IGC_OK: return "IGC_OK";
+        case IGC_ERR_INVALID_VALUE: return "IGC_ERR_INVALID_VALUE: invalid size, leading dimension, enum or pointer";
+        case IGC_ERR_MISALIGNED: return "IGC_ERR_MISALIGNED: pointer or leading dimension not 16-byte aligned";
+        case IGC_ERR_UNSUPPORTED: return "IGC_ERR_UNSUPPORTED: configuration not compiled or operand too large";
+        case IGC_ERR_HIP: return "IGC_ERR_HIP: the HIP runtime failed to launch the kernel";
+    }
+    return "unknown igc_status_t";
+}
+
+int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chunk) {
+    if (row < 0 || logical_chunk < 0 || logical_chunk >= chunks_per_row) return -1;
+    if (k_contiguous) {
+        if (chunks_per_row == 8) return logical_chunk ^ swz_k<8>(row);
+        if (chunks_per_row == 4) return logical_chunk ^ swz_k<4>(row);
+        return -1;
+    }
+    if (chunks_per_row < 16 || chunks_per_row % 16 != 0) return -1;
+    return logical_chunk ^ swz_mn(row);
+}
+
+int igc_ring_schedule(int D, int KT, int* ev, int cap) {
+    if (D < 1 || D > 8 || KT < 0 || cap < 0 || (cap > 0 && !ev)) return -1;
+    int n = 0;
+    auto emit = [&](int kind, int tile, int slot) {
+        if (n < cap) {
+            ev[3 * n] = kind;
+            ev[3 * n + 1] = tile;
+            ev[3 * n + 2] = slot;
+        }
+        ++n;
+    };
+    enum { ISSUE = 0, WAIT = 1, READ = 2, BARRIER = 3 };
+    if (D >= 2) {
+        // the K loop is padded to a multiple of D with zero-filled tiles
+        const int KTp = (KT + D - 1) / D * D;
+        for (int s = 0; s < D; ++s)
+            if (s < KTp) emit(ISSUE, s, Ring::slot(D, s));
+        if (KTp > 0) {
+            emit(WAIT, 0, Ring::inflight_after(D, KTp, 0));
+            emit(READ, 0, Ring::slot(D, 0));
+        }
+        for (int t = 0; t < KTp; ++t) {
+            if (t + 1 < KTp) {
+                emit(WAIT, t + 1, Ring::inflight_after(D, KTp, t + 1));
+                if (t + D < KTp) emit(ISSUE, t + D, Ring::slot(D, t + D));
+                emit(READ, t + 1, Ring::slot(D, t + 1));
+            } else {
+                emit(BARRIER, t, 0);  // drained; the kernel's trailing read is of no tile
+            }
+        }
+    } else {
+        if (KT > 0) {
+            emit(ISSUE, 0, 0);
+            emit(WAIT, 0, 0);
+            emit(READ, 0, 0);
+        }
+        for (int t = 0; t < KT; ++t) {
+            emit(BARRIER, t, 0);
+            if (t + 1 < KT) {
+                emit(ISSUE, t + 1, 0);
+                emit(WAIT, t + 1, 0);
+                emit(READ, t + 1, 0);
+            } else {
+                emit(BARRIER, t, 0);
+            }
+        }
+    }
+    return n;
+}
+
+}  // extern "C"

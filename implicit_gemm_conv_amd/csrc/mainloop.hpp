@@ -1,0 +1,672 @@
+// mainloop.hpp -- the software-pipelined bf16/fp16 MFMA mainloop for gfx950.
+//
+// One workgroup of 4 wave64s computes a BM x BN tile of C = A * B (or of the
+// implicit-GEMM view of an NHWC convolution).  Waves form a 2 x 2 grid; each
+// owns a (BM/2) x (BN/2) sub-tile held as 32x32 MFMA blocks of fp32
+// accumulators in registers for the whole K loop.
+//
+// Subsystems (the "B200 TMA Pipeline Designer" page, Executable steps 2-7,
+// re-done for CDNA4):
+//  1. Stage ring: PIPE_DEPTH LDS stages, each its own __shared__ array so that
+//     every slot index is a compile-time constant after unrolling the K loop by
+//     PIPE_DEPTH; the compiler then proves the direct-to-LDS writes into one
+//     slot do not alias the ds_reads of another and emits no conservative
+//     vmcnt(0).  Operand tiles move global -> LDS with buffer_load_dwordx4 ...
+//     lds (16 B per lane, written at M0 + 16*lane), one 1 KB wave instruction
+//     at a time; out-of-range chunks get an out-of-bounds buffer offset and
+//     land as zeros (the tile boundary policy).  Schedule: ring.hpp.
+//  2. Swizzle: the direct-to-LDS destination is fixed, so the XOR swizzle is
+//     applied on the global side (which 16-byte chunk each lane fetches) and
+//     undone by the fragment reader with the same map.  K-contiguous tiles
+//     (rows of BK elements) XOR the chunk index with (row&7)^((row>>3)&1)
+//     for BK = 64, or ((row>>1)^(row>>3))&3 for BK = 32;
+//     M/N-contiguous tiles (rows of BM or BN elements, read with the
+//     transposing ds_read_b64_tr_b16) XOR it with {0,6,12,10}[row&3].  Both make
+//     the 8- and 16-lane phases of a fragment read hit distinct banks.
+//  3. MFMA loop: v_mfma_f32_32x32x16_{bf16,f16}; each lane holds 8 consecutive
+//     k of one row/column per operand.  B is passed as the first operand so
+//     that each lane's 4 consecutive accumulators are 4 consecutive output
+//     columns (vector stores in the epilogue).
+//  4. Boundary: rows/columns past M/N and k past K load as zeros; when K is not
+//     a multiple of 8 the lane that loaded a chunk straddling K zeroes its tail
+//     in LDS after its own wait and before the barrier.  The epilogue stores
+//     only in-range elements (full tiles take an unmasked vector path).
+//  5. im2col: for the convolution, each A row (output pixel n,p,q) and K chunk
+//     (tap r,s and 8 channels) maps to x[n][p*sh-ph+r*dh][q*sw-pw+s*dw][c..c+7],
+//     or to the out-of-bounds offset when the tap falls in the zero padding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ring.hpp"
+
+namespace igc {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
+#define IGC_LDS __attribute__((address_space(3)))
+
+template <int I>
+struct IntC {
+    static constexpr int value = I;
+    constexpr operator int() const { return I; }
+};
+// Calls f(IntC<B>{}), ..., f(IntC<E-1>{}): the index is a compile-time constant in the body.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kOob = 0x80000000u;          // buffer offset that is always out of range
+constexpr int kNumRecords = 0x7fffffff;         // range of every buffer resource
+constexpr int kRsrcFlags = 0x00020000;          // gfx9 raw buffer: 32-bit dword format
+
+enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
+struct Params {
+    const void* A;   // GEMM A, or conv x (NHWC)
+    const void* B;   // GEMM B, or conv w (KRSC)
+    void* C;         // row-major M x N (conv: NPQK)
+    int64_t M, N, K; // GEMM view
+    int64_t lda, ldb, ldc;
+    int tiles_m, tiles_n;
+    int out_kind;
+    int k_ragged8;   // K % 8 != 0: chunk straddling K must be zeroed
+    int vec_ok;      // output rows allow 8/16-byte vector stores
+    // convolution geometry (CONV instances only)
+    int H, W, Cin, R, S, P, Q, sh, sw, ph, pw, dh, dw;
+};
+
+// XOR swizzle of the 16-byte chunk index within a K-contiguous LDS row of CPR
+// chunks.  A fragment read has 8 or 16 consecutive lanes on consecutive rows at
+// the same logical chunk; the map sends each such group to distinct 16-byte
+// bank groups, whether the LDS serves 128 or 256 bytes per cycle.
+template <int CPR>
+IGC_HD inline int swz_k(int row) {
+    static_assert(CPR == 8 || CPR == 4, "K tile of 64 or 32 elements");
+    if constexpr (CPR == 8) {
+        return (row & 7) ^ ((row >> 3) & 1);  // 128-byte rows
+    } else {
+        return ((row >> 1) ^ (row >> 3)) & 3;  // 64-byte rows, two per 128 bytes
+    }
+}
+// XOR swizzle of the 16-byte chunk index within an M/N-contiguous LDS row.
+IGC_HD inline int swz_mn(int row) { return (0xAC60 >> ((row & 3) * 4)) & 0xF; }  // {0,6,12,10}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords, kRsrcFlags);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, IGC_LDS void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4]<<14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }  // lgkmcnt(0) only
+
+// MFMA 32x32x16, fp32 accumulate.
+template <bool FP16>
+__device__ __forceinline__ f32x16_t mfma(i16x8_t a, i16x8_t b, f32x16_t c) {
+    if constexpr (FP16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Operand tile geometry.  ROWS = BM (operand A) or BN (operand B).
+//   KC = true : LDS tile is ROWS rows of BK elements (K contiguous).
+//   KC = false: LDS tile is BK rows of ROWS elements (M or N contiguous).
+// ---------------------------------------------------------------------------
+template <int ROWS, int BK, bool KC>
+struct Tile {
+    static constexpr int BYTES = ROWS * BK * 2;
+    static constexpr int INSTR = BYTES / 1024;        // 1 KB wave instructions per stage
+    static constexpr int IPW = INSTR / kWaves;        // per wave
+    static constexpr int ROW_ELEMS = KC ? BK : ROWS;  // elements per LDS row
+    static constexpr int CPR = ROW_ELEMS / 8;         // 16-byte chunks per LDS row
+    static constexpr int RPI = 64 / CPR;              // LDS rows per wave instruction
+    static_assert(BYTES % (1024 * kWaves) == 0, "tile must split into whole wave instructions");
+    static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row must be 8..512 elements");
+    // LDS row, physical chunk and logical chunk written by `lane` in wave instruction q.
+    __device__ static int row_of(int q, int lane) { return q * RPI + lane / CPR; }
+    __device__ static int logical_chunk(int q, int lane) {
+        const int row = row_of(q, lane);
+        if constexpr (KC) {
+            return (lane % CPR) ^ swz_k<CPR>(row);
+        } else {
+            return (lane % CPR) ^ swz_mn(row);
+        }
+    }
+};
+
+template <bool FP16_, int BM_, int BN_, int BK_, int D_, bool A_KC_, bool B_KC_, bool CONV_>
+struct Cfg {
+    static constexpr bool FP16 = FP16_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, D = D_;
+    static constexpr bool A_KC = A_KC_, B_KC = B_KC_, CONV = CONV_;
+    static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave sub-tile
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int KK = BK / 16;                // MFMA k-steps per K tile
+    using TA = Tile<BM, BK, A_KC>;
+    using TB = Tile<BN, BK, B_KC>;
+    static constexpr int STAGE_BYTES = TA::BYTES + TB::BYTES;
+    static constexpr int LDS_BYTES = STAGE_BYTES * D;
+    static constexpr int LPT = TA::IPW + TB::IPW;     // loads per K tile per wave
+    static_assert(!CONV || A_KC, "im2col operand is channel (K) contiguous");
+    static_assert(KK % 2 == 0, "fragment double-buffer parity needs an even number of k-steps");
+    static_assert(D >= 1 && D <= 8, "pipe depth");
+    static_assert(LDS_BYTES <= 163840, "stage ring exceeds the 160 KB of LDS per CU");
+    static_assert(D < 2 || (D - 2) * LPT < 64, "vmcnt cannot express that many loads in flight");
+};
+
+// Per-lane DMA state of one operand: offsets of the chunks this lane fetches
+// for each of its wave instructions, relative to a per-tile buffer base.
+template <int IPW>
+struct DmaState {
+    uint32_t voff[IPW];
+};
+
+// ---------------------------------------------------------------------------
+// The kernel body.
+// ---------------------------------------------------------------------------
+template <class C>
+struct Mainloop {
+    using TA = typename C::TA;
+    using TB = typename C::TB;
+    static constexpr int BM = C::BM, BN = C::BN, BK = C::BK, D = C::D, KK = C::KK;
+    static constexpr int FM = C::FM, FN = C::FN;
+
+    // ---- per-workgroup setup -------------------------------------------------
+    const Params p;  // a copy: kernel arguments stay in scalar registers
+    int lane, wave, wm, wn;
+    int64_t m0, n0;  // tile origin
+    int KT;          // number of K tiles
+    int KTp;         // KT rounded up to a multiple of D (phantom tiles load zeros)
+    DmaState<TA::IPW> da;
+    DmaState<TB::IPW> db;
+    // im2col: per A instruction, the pixel base offset and top-left input coordinate
+    int conv_pix[C::CONV ? TA::IPW : 1];
+    int conv_h0[C::CONV ? TA::IPW : 1];
+    int conv_w0[C::CONV ? TA::IPW : 1];
+    // fragment read offsets (bytes within a stage's operand region)
+    uint32_t fa_off[C::A_KC ? KK : FM];
+    uint32_t fb_off[C::B_KC ? KK : FN];
+
+    __device__ __forceinline__ Mainloop(const Params p_, int64_t m0_, int64_t n0_) : p(p_), m0(m0_), n0(n0_) {
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        wm = wave >> 1;
+        wn = wave & 1;
+        KT = (int)((p.K + BK - 1) / BK);
+        KTp = (KT + D - 1) / D * D;
+        setup_dma();
+        setup_frag_offsets();
+    }
+
+    __device__ __forceinline__ void setup_dma() {
+        // Operand A
+#pragma unroll
+        for (int j = 0; j < TA::IPW; ++j) {
+            const int q = j * kWaves + wave;
+            const int row = TA::row_of(q, lane);
+            const int c = TA::logical_chunk(q, lane);
+            if constexpr (C::CONV) {
+                const int64_t m = m0 + row;
+                const int PQ = p.P * p.Q;
+                const int mm = (int)(m < p.M ? m : 0);
+                const int n = mm / PQ, pq = mm - n * PQ;
+                const int pp = pq / p.Q, qq = pq - pp * p.Q;
+                conv_pix[j] = n * p.H * p.W * p.Cin;
+                conv_h0[j] = m < p.M ? pp * p.sh - p.ph : -(1 << 28);  // invalid rows never hit the image
+                conv_w0[j] = qq * p.sw - p.pw;
+                da.voff[j] = 0;
+            } else if constexpr (C::A_KC) {
+                // A row-major: tile row = m, chunk c covers k = 8c .. 8c+7 of the current K tile
+                const bool ok = m0 + row < p.M;
+                da.voff[j] = ok ? (uint32_t)(row * p.lda * 2 + c * 16) : kOob;
+            } else {
+                // A column-major: LDS row = k, chunk c covers m = m0 + 8c .. +7
+                const bool ok = m0 + 8 * c < p.M;
+                da.voff[j] = ok ? (uint32_t)(row * p.lda * 2 + c * 16) : kOob;
+            }
+        }
+        // Operand B
+#pragma unroll
+        for (int j = 0; j < TB::IPW; ++j) {
+            const int q = j * kWaves + wave;
+            const int row = TB::row_of(q, lane);
+            const int c = TB::logical_chunk(q, lane);
+            if constexpr (C::B_KC) {
+                // B column-major (N x K storage): tile row = n
+                const bool ok = n0 + row < p.N;
+                db.voff[j] = ok ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOob;
+            } else {
+                // B row-major (K x N storage): LDS row = k, chunk c covers n = n0 + 8c .. +7
+                const bool ok = n0 + 8 * c < p.N;
+                db.voff[j] = ok ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOob;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void setup_frag_offsets() {
+        if constexpr (C::A_KC) {
+            // lane reads row (wm*WTM + 32i + lane%32), logical chunk 2*kk + lane/32
+            const int row = wm * C::WTM + (lane & 31);
+            const int x = (lane >> 5) ^ swz_k<TA::CPR>(row);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fa_off[kk] = row * BK * 2 + (((2 * kk) ^ x) * 16);
+        } else {
+            const int g = lane >> 4, i16 = lane & 15;
+            const int rowpart = 8 * (g >> 1) + (i16 >> 2);
+            const int u = 2 * (g & 1) + ((i16 & 3) >> 1);
+            const int s = swz_mn(i16 >> 2);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int cl = (wm * C::WTM) / 8 + 4 * i + u;
+                fa_off[i] = rowpart * BM * 2 + ((cl ^ s) * 16) + 8 * (i16 & 1);
+            }
+        }
+        if constexpr (C::B_KC) {
+            const int row = wn * C::WTN + (lane & 31);
+            const int x = (lane >> 5) ^ swz_k<TB::CPR>(row);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) fb_off[kk] = row * BK * 2 + (((2 * kk) ^ x) * 16);
+        } else {
+            const int g = lane >> 4, i16 = lane & 15;
+            const int rowpart = 8 * (g >> 1) + (i16 >> 2);
+            const int u = 2 * (g & 1) + ((i16 & 3) >> 1);
+            const int s = swz_mn(i16 >> 2);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int cl = (wn * C::WTN) / 8 + 4 * j + u;
+                fb_off[j] = rowpart * BN * 2 + ((cl ^ s) * 16) + 8 * (i16 & 1);
+            }
+        }
+    }
+
+    // ---- global -> LDS: issue every load of K tile t into the given stage ----
+    // TAIL: t is the last K tile and K % BK != 0, so chunks past K are masked.
+    template <bool TAIL>
+    __device__ __forceinline__ void issue_tile(int t, IGC_LDS char* stage) {
+        const int64_t k0 = (int64_t)t * BK;
+        constexpr bool tail = TAIL;
+        IGC_LDS char* sa = stage;
+        IGC_LDS char* sb = stage + TA::BYTES;
+        // ---- A
+        if constexpr (C::CONV) {
+            const char* xb = (const char*)p.A;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(xb);
+            const bool uniform_tap = (p.Cin % BK) == 0;
+            int r = 0, s = 0, cbase = 0;
+            if (uniform_tap) {
+                const int tap = (int)(k0 / p.Cin);
+                r = tap / p.S;
+                s = tap - r * p.S;
+                cbase = (int)(k0 - (int64_t)tap * p.Cin);
+            }
+#pragma unroll
+            for (int j = 0; j < TA::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                const int c = TA::logical_chunk(q, lane);
+                int rr = r, ss = s, cin = cbase + 8 * c;
+                bool kok = !tail || k0 + 8 * c < p.K;
+                if (!uniform_tap) {
+                    const int kg = (int)k0 + 8 * c;
+                    kok = kok && kg < p.K;
+                    const int tap = kg / p.Cin;
+                    cin = kg - tap * p.Cin;
+                    rr = tap / p.S;
+                    ss = tap - rr * p.S;
+                }
+                const int h = conv_h0[j] + rr * p.dh;
+                const int w = conv_w0[j] + ss * p.dw;
+                const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+                const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
+                dma16(rs, sa + q * 1024, ok ? off : kOob);
+            }
+        } else if constexpr (C::A_KC) {
+            const char* base = (const char*)p.A + (m0 * p.lda + k0) * 2;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+            for (int j = 0; j < TA::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                uint32_t off = da.voff[j];
+                if (tail && k0 + 8 * TA::logical_chunk(q, lane) >= p.K) off = kOob;
+                dma16(rs, sa + q * 1024, off);
+            }
+        } else {
+            const char* base = (const char*)p.A + (k0 * p.lda + m0) * 2;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+            for (int j = 0; j < TA::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                uint32_t off = da.voff[j];
+                if (tail && k0 + TA::row_of(q, lane) >= p.K) off = kOob;
+                dma16(rs, sa + q * 1024, off);
+            }
+        }
+        // ---- B
+        if constexpr (C::B_KC) {
+            const char* base = (const char*)p.B + (n0 * p.ldb + k0) * 2;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+            for (int j = 0; j < TB::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                uint32_t off = db.voff[j];
+                if (tail && k0 + 8 * TB::logical_chunk(q, lane) >= p.K) off = kOob;
+                dma16(rs, sb + q * 1024, off);
+            }
+        } else {
+            const char* base = (const char*)p.B + (k0 * p.ldb + n0) * 2;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+            for (int j = 0; j < TB::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                uint32_t off = db.voff[j];
+                if (tail && k0 + TB::row_of(q, lane) >= p.K) off = kOob;
+                dma16(rs, sb + q * 1024, off);
+            }
+        }
+    }
+
+    // Tiles t >= KT are phantom tiles (the K loop is rounded up to a multiple
+    // of the ring depth): every one of their loads is out of bounds, so the
+    // slot fills with zeros and the MFMAs on it add exact zeros.
+    __device__ __forceinline__ void issue(int t, IGC_LDS char* stage) {
+        if ((int64_t)(t + 1) * BK > p.K)
+            issue_tile<true>(t, stage);
+        else
+            issue_tile<false>(t, stage);
+    }
+
+    // After this wave's loads of K tile t have landed and before the barrier:
+    // when K % 8 != 0, the chunk straddling K holds elements k >= K read from
+    // beyond the row's end; the lane that fetched it zeroes them.
+    __device__ __forceinline__ void fixup_ragged_k(int t, IGC_LDS char* stage) {
+        const int64_t k0 = (int64_t)t * BK;
+        if (!p.k_ragged8 || k0 + BK <= p.K) return;
+        // the only chunk that straddles K is the one starting at k0 + 8*cs
+        const int cs = (int)((p.K - k0) >> 3);
+        const int keep = (int)((p.K - k0) & 7);  // elements of that chunk below K
+        // bytes of the 16-byte chunk to keep: the first 2*keep
+        const uint32_t m0w = keep >= 2 ? 0xffffffffu : (keep == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m1w = keep >= 4 ? 0xffffffffu : (keep == 3 ? 0x0000ffffu : 0u);
+        const uint32_t m2w = keep >= 6 ? 0xffffffffu : (keep == 5 ? 0x0000ffffu : 0u);
+        const uint32_t m3w = keep == 7 ? 0x0000ffffu : 0u;
+        auto fix = [&](IGC_LDS char* region, int q, int c) __attribute__((always_inline)) {
+            if (c == cs) {
+                typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+                IGC_LDS u32x4_t* e = (IGC_LDS u32x4_t*)(region + q * 1024 + lane * 16);
+                u32x4_t v = *e;
+                v[0] &= m0w;
+                v[1] &= m1w;
+                v[2] &= m2w;
+                v[3] &= m3w;
+                *e = v;
+            }
+        };
+        if constexpr (C::A_KC && !C::CONV) {
+#pragma unroll
+            for (int j = 0; j < TA::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                fix(stage, q, TA::logical_chunk(q, lane));
+            }
+        }
+        if constexpr (C::B_KC) {
+#pragma unroll
+            for (int j = 0; j < TB::IPW; ++j) {
+                const int q = j * kWaves + wave;
+                fix(stage + TA::BYTES, q, TB::logical_chunk(q, lane));
+            }
+        }
+    }
+
+    // ---- LDS -> registers: fragments of one MFMA k-step ----------------------
+    __device__ __forceinline__ void read_frags(const IGC_LDS char* stage, int kk, i16x8_t (&fa)[FM], i16x8_t (&fb)[FN]) {
+        const IGC_LDS char* sa = stage;
+        const IGC_LDS char* sb = stage + TA::BYTES;
+        if constexpr (C::A_KC) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *(const IGC_LDS i16x8_t*)(sa + fa_off[kk] + i * 32 * BK * 2);
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const IGC_LDS char* a0 = sa + fa_off[i] + (16 * kk) * BM * 2;
+                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)a0);
+                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(a0 + 4 * BM * 2));
+                fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+        if constexpr (C::B_KC) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *(const IGC_LDS i16x8_t*)(sb + fb_off[kk] + j * 32 * BK * 2);
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const IGC_LDS char* b0 = sb + fb_off[j] + (16 * kk) * BN * 2;
+                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)b0);
+                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(b0 + 4 * BN * 2));
+                fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void mma(f32x16_t (&acc)[FM][FN], const i16x8_t (&fa)[FM], const i16x8_t (&fb)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma<C::FP16>(fb[j], fa[i], acc[i][j]);
+    }
+
+    // Wait until at most n later K tiles of this wave's loads are still in
+    // flight (n in [0, D-2]); loads complete in issue order, so the oldest
+    // outstanding tile has then landed.
+    template <int V>
+    __device__ __forceinline__ static void wait_tiles(int n) {
+        if constexpr (V <= 0) {
+            wait_vmcnt<0>();
+        } else {
+            if (n >= V) {
+                wait_vmcnt<V * C::LPT>();
+            } else {
+                wait_tiles<V - 1>(n);
+            }
+        }
+    }
+
+    // ---- epilogue: accumulators -> C ---------------------------------------
+    __device__ __forceinline__ void store(const f32x16_t (&acc)[FM][FN]) {
+        const bool full = p.vec_ok && (m0 + BM <= p.M) && (n0 + BN <= p.N);
+        const int64_t mrow = m0 + wm * C::WTM + (lane & 31);
+        const int64_t ncol = n0 + wn * C::WTN + 4 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = mrow + 32 * i;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                // one 32x32 block at a time: only 16 accumulators move to VGPRs at once
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t n = ncol + 32 * j + 8 * g;
+                    const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                    const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                    const int64_t off = m * p.ldc + n;
+                    if (full) {
+                        if (p.out_kind == OUT_F32) {
+                            *(f32x4_t*)((float*)p.C + off) = f32x4_t{v0, v1, v2, v3};
+                        } else if (p.out_kind == OUT_BF16) {
+                            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+                            *(bf16x4_t*)((__bf16*)p.C + off) = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                        } else {
+                            typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+                            *(f16x4_t*)((_Float16*)p.C + off) =
+                                f16x4_t{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+                        }
+                    } else if (m < p.M) {
+                        const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (n + e < p.N) {
+                                if (p.out_kind == OUT_F32)
+                                    ((float*)p.C)[off + e] = v[e];
+                                else if (p.out_kind == OUT_BF16)
+                                    ((__bf16*)p.C)[off + e] = (__bf16)v[e];
+                                else
+                                    ((_Float16*)p.C)[off + e] = (_Float16)v[e];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+};
+
+}  // namespace igc
+
+namespace igc {
+
+// Compiler-level memory ordering point (emits no instruction).  The hardware
+// ordering comes from the explicit s_waitcnt and s_barrier around it.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Every wave has drained its own LDS reads (and, before that, waited for its
+// own direct-to-LDS loads); then the workgroup meets.
+__device__ __forceinline__ void ring_barrier() {
+    wait_lgkmcnt0();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+// blockIdx -> (tile_m, tile_n).  Workgroup i is dispatched to XCD i % 8, and
+// each XCD has its own L2: give every XCD a contiguous range of tile ids, and
+// walk that range GROUP_M tiles down M at a time so the tiles resident on one
+// XCD share A rows and B columns in its L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+    constexpr int kXcds = 8, kGroupM = 4;
+    const int G = tiles_m * tiles_n;
+    const int wg = blockIdx.x;
+    const int q = G / kXcds, r = G % kXcds, x = wg % kXcds, i = wg / kXcds;
+    const int id = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    const int group = kGroupM * tiles_n;
+    const int g = id / group;
+    const int first_m = g * kGroupM;
+    const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+    const int in = id - g * group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+}
+
+// LDS slot U of the stage ring of configuration C: one __shared__ array per
+// slot, so every slot is a distinct object to the compiler.
+template <class C, int U>
+__device__ __forceinline__ IGC_LDS char* stage() {
+    __shared__ __attribute__((aligned(1024))) char buf[C::STAGE_BYTES];
+    return (IGC_LDS char*)buf;
+}
+
+template <class C>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
+    using ML = Mainloop<C>;
+    constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN;
+
+    int tm, tn;
+    tile_coords(p.tiles_m, p.tiles_n, tm, tn);
+    ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN);
+    const int KT = ml.KT, KTp = ml.KTp;
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+    i16x8_t fa[2][FM], fb[2][FN];
+
+    // The accumulators are never updated under a branch: every K tile of the
+    // padded loop runs the same MFMA sequence, so no copies of them are needed.
+    if constexpr (D >= 2) {
+        // ---- prologue: fill the ring
+        static_for<0, D>([&](auto S) __attribute__((always_inline)) {
+            if (S < KTp) ml.issue(S, stage<C, S>());
+        });
+        ml.template wait_tiles<D - 1>(Ring::inflight_after(D, KTp, 0));
+        ml.fixup_ragged_k(0, stage<C, 0>());
+        ring_barrier();
+        ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+        // ---- steady state, unrolled by D so every slot is a constant
+        for (int t0 = 0; t0 < KTp; t0 += D) {
+            static_for<0, D>([&](auto U) __attribute__((always_inline)) {
+                constexpr int u = U;
+                constexpr int un = (u + 1) % D;
+                const int t = t0 + u;
+                static_for<0, KK - 1>([&](auto KS) __attribute__((always_inline)) {
+                    constexpr int kk = KS;
+                    ml.read_frags(stage<C, u>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                    ML::mma(acc, fa[kk & 1], fb[kk & 1]);
+                    __builtin_amdgcn_sched_barrier(0);  // k-steps stay in order: two fragment sets live
+                });
+                // ready(t+1): own loads landed, then everyone; free(t): all reads of t done.
+                // After the last tile this is a harmless extra barrier and read.
+                ml.template wait_tiles<D - 2>(Ring::inflight_after(D, KTp, t + 1));
+                ml.fixup_ragged_k(t + 1, stage<C, un>());
+                ring_barrier();
+                if (t + D < KTp) ml.issue(t + D, stage<C, u>());
+                ml.read_frags(stage<C, un>(), 0, fa[0], fb[0]);
+                ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    } else {
+        // ---- D == 1: one slot, no overlap of loads with compute
+        if (KT > 0) ml.issue(0, stage<C, 0>());
+        wait_vmcnt<0>();
+        ml.fixup_ragged_k(0, stage<C, 0>());
+        ring_barrier();
+        ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+        for (int t = 0; t < KT; ++t) {
+            static_for<0, KK - 1>([&](auto KS) __attribute__((always_inline)) {
+                constexpr int kk = KS;
+                ml.read_frags(stage<C, 0>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                ML::mma(acc, fa[kk & 1], fb[kk & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            ring_barrier();  // free: every wave has read tile t
+            if (t + 1 < KT) ml.issue(t + 1, stage<C, 0>());
+            wait_vmcnt<0>();
+            ml.fixup_ragged_k(t + 1, stage<C, 0>());
+            ring_barrier();  // ready: tile t+1 landed for every wave
+            ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+            ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // ---- output epilogue: nothing is in flight any more
+    ml.store(acc);
+}
+
+}  // namespace igc

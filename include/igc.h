@@ -1,0 +1,170 @@
+/*
+ * igc.h -- C ABI of libigc: a software-pipelined bf16/fp16 GEMM with fp32
+ * accumulation, and the same mainloop run as an implicit-GEMM (im2col) NHWC
+ * convolution, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows the "B200 TMA Pipeline Designer" page ("Executable
+ * steps": a tiled matrix product fed by a ring of PIPE_DEPTH shared-memory
+ * stages under ready/free synchronisation, with a prologue / steady-state /
+ * epilogue timeline) and the "two free pipeline stages" note (section "The atom
+ * changes the fragment": the same pipelined mainloop driving an implicit-GEMM
+ * convolution with IM2COL operand loads).  The pages' NVIDIA mechanisms (TMA
+ * descriptors, mbarriers, elected issuer lanes, 2-SM atoms) are not used; the
+ * library uses gfx950 direct-to-LDS buffer loads, s_waitcnt/s_barrier and MFMA.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or retains them and keeps no per-call state; calls
+ *   are thread-safe.
+ * - Each call only validates its arguments and enqueues work on `stream`
+ *   (a hipStream_t; NULL = the default stream).  It returns before the GPU
+ *   finishes; synchronise the stream to observe the result.
+ * - Leading dimensions are in ELEMENTS, not bytes.
+ * - Alignment: every tensor base pointer must be 16-byte aligned and every
+ *   leading dimension times the element size must be a multiple of 16 bytes
+ *   (8 elements for 16-bit types, 4 for fp32).  Otherwise IGC_ERR_MISALIGNED.
+ * - Arguments are checked before anything is launched; on any error nothing
+ *   is enqueued and the output is untouched.  No exception crosses the ABI.
+ * - Outputs must not alias inputs (not checked; the result is undefined).
+ * - Results are deterministic: the same inputs give the same bits on every
+ *   call (no atomics; a fixed summation order per output element).
+ */
+#ifndef IGC_H
+#define IGC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *igc_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    IGC_OK = 0,
+    IGC_ERR_INVALID_VALUE = 1, /* negative size, leading dimension too small, bad enum, NULL pointer */
+    IGC_ERR_MISALIGNED = 2,    /* pointer or leading dimension breaks the 16-byte rule; conv C % 8 != 0 */
+    IGC_ERR_UNSUPPORTED = 3,   /* tuning choice not compiled in, or an operand span >= 2^31 bytes */
+    IGC_ERR_HIP = 4            /* the HIP runtime reported an error when launching */
+} igc_status_t;
+
+typedef enum { IGC_ROW_MAJOR = 0, IGC_COL_MAJOR = 1 } igc_layout_t;
+
+typedef enum { IGC_OUT_F32 = 0, IGC_OUT_BF16 = 1, IGC_OUT_F16 = 2 } igc_out_t;
+
+/* Optional tuning: output tile BM x BN, K tile BK, and PIPE_DEPTH = number of
+ * LDS stages in the ring.  Only compiled combinations are accepted (see
+ * igc_tune_supported); NULL selects the built-in choice for the shape. */
+typedef struct {
+    int bm, bn, bk, pipe_depth;
+} igc_tune_t;
+
+/*
+ * C = A * B with bf16 inputs, fp32 accumulation, output type `c_type`.
+ *   A is M x K: IGC_ROW_MAJOR -> A[i*lda + k] (lda >= K);
+ *               IGC_COL_MAJOR -> A[k*lda + i] (lda >= M).
+ *   B is K x N: IGC_ROW_MAJOR -> B[k*ldb + j] (ldb >= N);
+ *               IGC_COL_MAJOR -> B[j*ldb + k] (ldb >= K).
+ *   C is M x N row-major: C[i*ldc + j] (ldc >= N), element type per c_type;
+ *     fp32 -> bf16/fp16 rounds to nearest-even.
+ * K == 0 writes zeros; M == 0 or N == 0 is a no-op returning IGC_OK.
+ */
+igc_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, igc_layout_t la,
+                       const void *B, int64_t ldb, igc_layout_t lb, void *C, int64_t ldc, igc_out_t c_type,
+                       igc_stream_t stream);
+
+/* Same contract as gemm_bf16 with IEEE binary16 (fp16) inputs. */
+igc_status_t gemm_fp16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, igc_layout_t la,
+                       const void *B, int64_t ldb, igc_layout_t lb, void *C, int64_t ldc, igc_out_t c_type,
+                       igc_stream_t stream);
+
+/* gemm_bf16 / gemm_fp16 with an explicit tile and pipeline depth (NULL = default). */
+igc_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, igc_layout_t la,
+                          const void *B, int64_t ldb, igc_layout_t lb, void *C, int64_t ldc, igc_out_t c_type,
+                          const igc_tune_t *tune, igc_stream_t stream);
+igc_status_t gemm_fp16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, igc_layout_t la,
+                          const void *B, int64_t ldb, igc_layout_t lb, void *C, int64_t ldc, igc_out_t c_type,
+                          const igc_tune_t *tune, igc_stream_t stream);
+
+/*
+ * Forward 2-D convolution (cross-correlation) as an implicit GEMM, bf16
+ * inputs, fp32 accumulation:
+ *   y[n][p][q][k] = sum_{r<R, s<S, c<C} x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c] * w[k][r][s][c]
+ * with zero padding (taps outside the H x W image contribute nothing).
+ *   x: NHWC, dense, N*H*W*C elements (bf16).
+ *   w: KRSC, dense, K*R*S*C elements (bf16).
+ *   y: NPQK, dense, N*P*Q*K elements of type y_type, where
+ *      P = (H + 2*ph - dh*(R-1) - 1)/sh + 1,  Q = (W + 2*pw - dw*(S-1) - 1)/sw + 1.
+ * Requirements: N, H, W, C, K, R, S >= 1 (N or K may be 0: no-op), strides and
+ * dilations >= 1, pads >= 0, P >= 1 and Q >= 1 (else IGC_ERR_INVALID_VALUE);
+ * C % 8 == 0 (else IGC_ERR_MISALIGNED); x must span < 2^31 bytes (else
+ * IGC_ERR_UNSUPPORTED).  The GEMM view is M = N*P*Q, N_gemm = K, K_gemm = R*S*C.
+ */
+igc_status_t conv2d_nhwc_implicit_gemm(int N, int H, int W, int C, int K, int R, int S, int stride_h,
+                                       int stride_w, int pad_h, int pad_w, int dil_h, int dil_w, const void *x,
+                                       const void *w, void *y, igc_out_t y_type, igc_stream_t stream);
+
+/* Same contract with IEEE binary16 (fp16) x and w. */
+igc_status_t conv2d_nhwc_implicit_gemm_fp16(int N, int H, int W, int C, int K, int R, int S, int stride_h,
+                                            int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                            const void *x, const void *w, void *y, igc_out_t y_type,
+                                            igc_stream_t stream);
+
+/* conv2d_nhwc_implicit_gemm with an explicit tile and pipeline depth (NULL = default);
+ * `fp16` selects binary16 inputs instead of bf16. */
+igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int R, int S, int stride_h,
+                                          int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                                          const void *x, const void *w, void *y, igc_out_t y_type, int fp16,
+                                          const igc_tune_t *tune, igc_stream_t stream);
+
+/* 1 if (bm, bn, bk, pipe_depth) is a compiled configuration, else 0. */
+int igc_tune_supported(const igc_tune_t *tune);
+
+/* Number of compiled configurations; igc_tune_get(i, &t) fills t for i in [0, count). */
+int igc_tune_count(void);
+int igc_tune_get(int i, igc_tune_t *out);
+
+/* LDS bytes one workgroup of the given configuration uses (0 if not compiled). */
+int64_t igc_tune_lds_bytes(const igc_tune_t *tune);
+
+/* Static text for a status code (never NULL). */
+const char *igc_status_string(igc_status_t status);
+
+/*
+ * Ring schedule of the mainloop, for inspection and testing on the host.
+ * For a K loop of `k_tiles` tiles and a ring of `pipe_depth` stages, writes up
+ * to `cap` events into `events` as int triples (kind, tile, slot):
+ *   kind 0 = issue the loads of `tile` into `slot`,
+ *   kind 1 = wait until `tile` has landed (each wave waits on its own loads,
+ *            then the workgroup barrier runs; `slot` is the value passed to the
+ *            wave's s_waitcnt vmcnt, i.e. how many of its loads may still be
+ *            in flight, counted in tiles),
+ *   kind 2 = read `tile` from `slot` (fragment loads + MFMA).
+ *   kind 3 = workgroup barrier only (D == 1 frees its single slot with it;
+ *            every schedule ends with one once nothing is left in flight).
+ * For pipe_depth >= 2 the K loop is padded to a multiple of pipe_depth with
+ * tiles whose loads are all out of range (they land as zeros and add nothing),
+ * so tiles up to that padded count appear.  Each wave drains its own LDS reads
+ * before every barrier, so a barrier after a tile's reads frees its slot.
+ * Returns the number of events (which may exceed cap), or -1 on bad input.
+ * This is the exact sequence the kernels execute.
+ */
+int igc_ring_schedule(int pipe_depth, int k_tiles, int *events, int cap);
+
+/*
+ * LDS swizzle of the operand tiles, for inspection and testing on the host.
+ * Operand tiles live in LDS as rows of 16-byte chunks; the chunk holding
+ * logical chunk `logical_chunk` of row `row` is stored at the returned
+ * physical chunk of the same row.  k_contiguous = 1: rows of the K tile
+ * (chunks_per_row = BK/8, 8 or 4); 0: rows of BM or BN elements read with the
+ * transposing LDS load (chunks_per_row a multiple of 16).  Returns -1 for an
+ * unsupported geometry.  These are the maps the kernels use.
+ */
+int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chunk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IGC_H */

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: every output element within |y - ref| <= 1e-4*S + 1e-6 (+ half an ulp of
+a 16-bit output format), S = sum |a*b|; bit-exact where the inputs make every
+partial sum exact.  Covers the five named workloads (the small one in full,
+the large ones on sampled outputs at full size in the benchmark's launch
+configuration), boundary tiles, K not a multiple of the K tile, varied K-tile
+counts for every compiled pipeline depth, all operand layouts, both input
+types, all output types, NaN padding that must never be read, and the
+convolution's padding/stride/dilation cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import implicit_gemm_conv_amd as igc
+from implicit_gemm_conv_amd import inputs
+import oracle
+from gpu_util import (LAYOUT, assert_close, oracle_gemm, round_to, run_conv, run_gemm, say)
+
+pytestmark = pytest.mark.gpu
+
+NAN_BITS = {"bf16": 0x7FC0, "fp16": 0x7E00}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    igc.lib()  # raises if the HIP library is missing: there is no fallback
+
+
+def nan_pad(bits, valid_cols, dtype):
+    """Fills the leading-dimension padding (columns >= valid_cols) with NaN."""
+    bits = bits.copy()
+    bits[:, valid_cols:] = NAN_BITS[dtype]
+    return bits
+
+
+def gemm_case(M, N, K, la, lb, dtype="bf16", out="f32", pad=8, seed=0, tune=None, dist=("uniform", 1.0)):
+    lda = (K if la == "row" else M) + pad
+    ldb = (N if lb == "row" else K) + pad
+    lda += (-lda) % 8
+    ldb += (-ldb) % 8
+    A, lda, B, ldb = inputs.gemm_operands(M, N, K, la, lb, lda, ldb, dtype, dist, dist, seed)
+    A = nan_pad(A, K if la == "row" else M, dtype)
+    B = nan_pad(B, N if lb == "row" else K, dtype)
+    y, _ = run_gemm(M, N, K, A, lda, la, B, ldb, lb, out=out, dtype=dtype, tune=tune)
+    ref, S = oracle_gemm(M, N, K, A, lda, la, B, ldb, lb, dtype)
+    return assert_close(y, ref, S, out, f"gemm {M}x{N}x{K} {la}/{lb} {dtype}->{out} tune={tune}")
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads
+# ---------------------------------------------------------------------------
+
+def test_workload_small_gemm_full():
+    cfg = inputs.WORKLOADS["gemm_bf16_128x96x200"]
+    A, lda, B, ldb = inputs.workload_operands("gemm_bf16_128x96x200")
+    say("workload gemm_bf16_128x96x200")
+    y, _ = run_gemm(cfg["M"], cfg["N"], cfg["K"], A, lda, cfg["la"], B, ldb, cfg["lb"], out=cfg["out"])
+    ref, S = oracle_gemm(cfg["M"], cfg["N"], cfg["K"], A, lda, cfg["la"], B, ldb, cfg["lb"])
+    r = assert_close(y, ref, S, cfg["out"], "gemm_bf16_128x96x200")
+    say(f"  max err/bound {r:.3g}")
+
+
+def sample_points(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, n))
+    cols = list(rng.integers(0, N, n))
+    # every element of the first and last 32 x 32 corner, and the last row / column
+    for r0, c0 in ((0, 0), (max(M - 32, 0), max(N - 32, 0)), (0, max(N - 32, 0)), (max(M - 32, 0), 0)):
+        for r in range(r0, min(r0 + 32, M)):
+            for c in range(c0, min(c0 + 32, N)):
+                rows.append(r)
+                cols.append(c)
+    for c in range(0, N, max(1, N // 512)):
+        rows.append(M - 1)
+        cols.append(c)
+    for r in range(0, M, max(1, M // 512)):
+        rows.append(r)
+        cols.append(N - 1)
+    return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
+@pytest.mark.parametrize("name,out", [
+    ("gemm_bf16_8192x8192x8192", None),
+    ("gemm_bf16_8192x8192x8192", "f32"),   # the accumulator itself at the strict bound
+    ("gemm_bf16_2048x1024x16384", None),
+    ("gemm_fp16_1000x1000x65536", None),
+])
+def test_workload_large_gemm_sampled(name, out):
+    cfg = inputs.WORKLOADS[name]
+    out = out or cfg["out"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    say(f"workload {name} -> {out}")
+    A, lda, B, ldb = inputs.workload_operands(name)
+    y, _ = run_gemm(M, N, K, A, lda, cfg["la"], B, ldb, cfg["lb"], out=out, dtype=cfg["dtype"])
+    rows, cols = sample_points(M, N, 12000, seed=cfg["seed"])
+    ref, S = oracle.gemm_sample(M, N, K, A, lda, LAYOUT[cfg["la"]], B, ldb, LAYOUT[cfg["lb"]],
+                                oracle.FP16 if cfg["dtype"] == "fp16" else oracle.BF16, rows, cols)
+    r = assert_close(y[rows, cols], ref, S, out, name)
+    say(f"  {rows.size} sampled outputs, max err/bound {r:.3g}")
+
+
+@pytest.mark.parametrize("out", [None, "f32"])
+def test_workload_conv_sampled(out):
+    name = "conv_bf16_n32_56x56_c256_k256_3x3"
+    cfg = inputs.WORKLOADS[name]
+    out = out or cfg["out"]
+    say(f"workload {name} -> {out}")
+    x, w = inputs.workload_operands(name)
+    geo = dict(sh=cfg["sh"], sw=cfg["sw"], ph=cfg["ph"], pw=cfg["pw"], dh=cfg["dh"], dw=cfg["dw"])
+    y, _ = run_conv(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], x, w, out=out, **geo)
+    rng = np.random.default_rng(4)
+    idx = list(rng.integers(0, y.size, 12000))
+    P, Q, K = y.shape[1], y.shape[2], y.shape[3]
+    # every output channel of the four image corners of the first and last image (padding taps)
+    for n in (0, cfg["N"] - 1):
+        for p in (0, P - 1):
+            for q in (0, Q - 1):
+                idx += [((n * P + p) * Q + q) * K + k for k in range(K)]
+    idx = np.array(idx, np.int64)
+    ref, S = oracle.conv2d_nhwc_sample(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], x, w,
+                                       oracle.BF16, idx, **geo)
+    r = assert_close(y.ravel()[idx], ref, S, out, name)
+    say(f"  {idx.size} sampled outputs, max err/bound {r:.3g}")
+
+
+# ---------------------------------------------------------------------------
+# boundary tiles, ragged K, layouts, types
+# ---------------------------------------------------------------------------
+
+SHAPES_MN = [(1, 1), (33, 257), (257, 33), (129, 129), (257, 257), (7, 300)]
+KS = [1, 8, 63, 64, 65, 200]
+
+
+@pytest.mark.parametrize("la,lb", [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")])
+def test_boundary_sweep(la, lb):
+    outs = ["f32", "bf16", "f16"]
+    i = 0
+    for (M, N) in SHAPES_MN:
+        for K in KS:
+            dtype = "fp16" if i % 3 == 2 else "bf16"
+            out = outs[i % 3]
+            say(f"boundary {M}x{N}x{K} {la}/{lb} {dtype}->{out}")
+            gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=100 + i)
+            i += 1
+
+
+def compiled_tunes():
+    return igc.tunes()
+
+
+@pytest.mark.parametrize("tune", [(256, 256, 64, 2), (256, 256, 32, 4), (256, 256, 64, 1), (256, 128, 64, 3),
+                                  (128, 128, 64, 4)])
+def test_k_tiles_sweep(tune):
+    """K_TILES in {1, D-1, D, D+1, 2D, 2D+1} plus a ragged tail, for each pipeline depth D."""
+    bm, bn, bk, d = tune
+    assert tune in compiled_tunes()
+    kts = sorted({1, max(d - 1, 1), d, d + 1, 2 * d, 2 * d + 1})
+    for j, kt in enumerate(kts):
+        for K in (kt * bk, kt * bk - 24):
+            if K <= 0:
+                continue
+            for (la, lb) in (("row", "row"), ("row", "col")):
+                say(f"tune {tune} K={K} ({la}/{lb})")
+                gemm_case(300, 270, K, la, lb, out="f32", seed=200 + j, tune=tune)
+
+
+@pytest.mark.parametrize("tune", [(256, 256, 64, 2), (256, 256, 32, 4), (256, 256, 64, 1), (256, 128, 64, 3),
+                                  (128, 128, 64, 4)])
+def test_k_chain_tags(tune):
+    """A = 1, b_kj = (floor(k/64) mod 5) + 1: C = sum_k tag(k) exactly.  Reading a stale ring slot (tile
+    t - D instead of t) changes the sum; dropping or repeating a K tile does too."""
+    bm, bn, bk, d = tune
+    for K in (bk * (2 * d + 3), 1000):
+        M, N = 130, 140
+        A = np.full((M, K), 0x3F80, np.uint16)
+        tags = np.array([(k // 64) % 5 + 1 for k in range(K)], np.float32)
+        B = torch.from_numpy(np.repeat(tags[:, None], N, axis=1)).to(torch.bfloat16).view(torch.int16).numpy()
+        B = B.view(np.uint16)
+        say(f"k-chain tune {tune} K={K}")
+        y, _ = run_gemm(M, N, K, A, K, "row", B, N, "row", out="f32", tune=tune)
+        assert np.all(y == float(tags.sum())), f"k-chain tune={tune} K={K}: {np.unique(y)[:5]}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_exact_integers_bit_exact(dtype, out):
+    """Integers in [-4, 4] with K*16 < 2^24: every partial sum is exact in fp32 in any order, so the GPU must
+    equal the oracle exactly (fp32 output) or the oracle rounded once to nearest-even (16-bit output)."""
+    for (M, N, K, la, lb) in ((512, 384, 1000, "row", "row"), (300, 200, 777, "col", "row"),
+                              (128, 96, 200, "row", "col"), (257, 129, 136, "col", "col")):
+        ld_a = K if la == "row" else M
+        ld_b = N if lb == "row" else K
+        ld_a += (-ld_a) % 8
+        ld_b += (-ld_b) % 8
+        A, lda, B, ldb = inputs.gemm_operands(M, N, K, la, lb, ld_a, ld_b, dtype, ("int", 4), ("int", 4), seed=7)
+        say(f"exact {M}x{N}x{K} {la}/{lb} {dtype}->{out}")
+        y, _ = run_gemm(M, N, K, A, lda, la, B, ldb, lb, out=out, dtype=dtype)
+        ref, _ = oracle_gemm(M, N, K, A, lda, la, B, ldb, lb, dtype)
+        want = round_to(ref, out)
+        bad = np.count_nonzero(y != want)
+        assert bad == 0, f"{bad} outputs differ from the exactly rounded oracle"
+
+
+def test_bf16_output_rounds_ties_to_even():
+    """Sums of exact integers that sit exactly half-way between two bf16 values must round to even."""
+    M, N = 64, 64
+    K = 64
+    # row i of A: 257 + 2*i split over K terms so the exact sum is odd and > 256 (bf16 ties)
+    A = np.zeros((M, K), np.float32)
+    for i in range(M):
+        target = 257 + 2 * i
+        A[i, 0] = target - 63 * 1.0
+        A[i, 1:] = 1.0
+    Ab = torch.from_numpy(A).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(torch.from_numpy(Ab.view(np.int16)).view(torch.bfloat16).float().numpy(), A)
+    B = np.full((K, N), 0x3F80, np.uint16)
+    y, _ = run_gemm(M, N, K, Ab, K, "row", B, N, "row", out="bf16")
+    ref, _ = oracle_gemm(M, N, K, Ab, K, "row", B, N, "row")
+    assert np.array_equal(y, round_to(ref, "bf16"))
+
+
+def test_k_zero_writes_zeros():
+    M, N = 70, 90
+    A = np.zeros((M, 8), np.uint16)
+    B = np.zeros((8, N), np.uint16)
+    y, _ = run_gemm(M, N, 0, A, 8, "row", B, 96, "row", out="f32")
+    assert np.all(y == 0)
+
+
+def test_deterministic_bits():
+    name = "gemm_bf16_2048x1024x16384"
+    cfg = inputs.WORKLOADS[name]
+    A, lda, B, ldb = inputs.workload_operands(name)
+    outs = [run_gemm(cfg["M"], cfg["N"], cfg["K"], A, lda, "row", B, ldb, "row", out="f32")[0] for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+# ---------------------------------------------------------------------------
+# convolution
+# ---------------------------------------------------------------------------
+
+CONV_CASES = [
+    # N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw
+    (2, 7, 9, 8, 5, 3, 3, 1, 1, 1, 1, 1, 1),
+    (1, 8, 6, 16, 4, 3, 3, 2, 2, 1, 1, 1, 1),     # stride 2
+    (2, 5, 5, 8, 3, 3, 3, 1, 1, 0, 0, 1, 1),      # no padding
+    (1, 9, 7, 8, 6, 3, 2, 1, 2, 2, 1, 2, 1),      # dilation, asymmetric filter and stride
+    (1, 7, 9, 8, 4, 2, 3, 1, 1, 1, 2, 1, 2),
+    (3, 1, 2, 24, 7, 3, 3, 1, 1, 1, 1, 1, 1),     # tiny image
+    (2, 3, 3, 64, 130, 3, 3, 1, 1, 1, 1, 1, 1),   # K not a multiple of 8
+    (2, 6, 5, 16, 9, 1, 1, 1, 1, 0, 0, 1, 1),     # 1x1
+    (4, 14, 14, 64, 64, 3, 3, 1, 1, 1, 1, 1, 1),  # C = BK: one tap per K tile
+    (2, 12, 10, 256, 256, 3, 3, 2, 1, 1, 1, 1, 1),
+    (1, 2, 3, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES)
+def test_conv_variants(case):
+    N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw = case
+    geo = dict(sh=sh, sw=sw, ph=ph, pw=pw, dh=dh, dw=dw)
+    for i, (dtype, out) in enumerate((("bf16", "f32"), ("fp16", "f16"), ("bf16", "bf16"))):
+        x, w = inputs.conv_operands(N, H, W, C, K, R, S, dtype, ("normal", 1.0), ("normal", 0.1), seed=31 + i)
+        say(f"conv {case} {dtype}->{out}")
+        y, _ = run_conv(N, H, W, C, K, R, S, x, w, out=out, dtype=dtype, **geo)
+        ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, R, S, x, w, oracle.FP16 if dtype == "fp16" else oracle.BF16,
+                                       **geo)
+        assert_close(y, ref, Sabs, out, f"conv {case} {dtype}->{out}")
+
+
+def test_conv_exact_integers():
+    N, H, W, C, K, R, S = 2, 9, 11, 32, 40, 3, 3
+    x, w = inputs.conv_operands(N, H, W, C, K, R, S, "bf16", ("int", 4), ("int", 4), seed=9)
+    y, _ = run_conv(N, H, W, C, K, R, S, x, w, ph=1, pw=1, out="f32")
+    ref, _ = oracle.conv2d_nhwc(N, H, W, C, K, R, S, x, w, oracle.BF16, ph=1, pw=1)
+    assert np.array_equal(y, ref)
+
+
+def test_conv_1x1_equals_gemm_on_gpu():
+    N, H, W, C, K = 2, 10, 12, 64, 48
+    x, w = inputs.conv_operands(N, H, W, C, K, 1, 1, "bf16", seed=12)
+    yc, _ = run_conv(N, H, W, C, K, 1, 1, x, w, out="f32")
+    yg, _ = run_gemm(N * H * W, K, C, x.reshape(-1, C), C, "row", w.reshape(K, C), C, "col", out="f32")
+    ref, S = oracle_gemm(N * H * W, K, C, x.reshape(-1, C), C, "row", w.reshape(K, C), C, "col")
+    assert_close(yc.reshape(-1, K), ref, S, "f32", "1x1 conv")
+    assert_close(yg, ref, S, "f32", "1x1 as gemm")
