@@ -175,7 +175,7 @@ def test_k_chain_tags(tune):
     t - D instead of t) changes the sum; dropping or repeating a K tile does too."""
     bm, bn, bk, d = tune
     for K in (bk * (2 * d + 3), 1000):
-        M, N = 130, 140
+        M, N = 130, 136  # row-major B: N * 2 bytes must be a multiple of 16
         A = np.full((M, K), 0x3F80, np.uint16)
         tags = np.array([(k // 64) % 5 + 1 for k in range(K)], np.float32)
         B = torch.from_numpy(np.repeat(tags[:, None], N, axis=1)).to(torch.bfloat16).view(torch.int16).numpy()
