@@ -56,12 +56,12 @@ def cpu_baseline(gcfg, ccfg, A, B, x, w):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
     M, N, K = gcfg["M"], gcfg["N"], gcfg["K"]
-    rows = 8
+    # calibrate on a slice, then size the slice to roughly 15 s of oracle work
+    rows = max(threads, 64)
     t0 = time.perf_counter()
     oracle.gemm(rows, N, K, A[:rows], K, oracle.ROW_MAJOR, B, N, oracle.ROW_MAJOR, oracle.BF16, threads=threads)
     t_probe = time.perf_counter() - t0
-    # grow the slice to roughly 10 s of oracle work
-    rows = int(min(M, max(rows, rows * 10.0 / max(t_probe, 1e-3))))
+    rows = int(min(M, rows * 15.0 / max(t_probe, 1e-3)))
     rows = max(threads, rows // threads * threads)
     t0 = time.perf_counter()
     oracle.gemm(rows, N, K, A[:rows], K, oracle.ROW_MAJOR, B, N, oracle.ROW_MAJOR, oracle.BF16, threads=threads)
@@ -89,6 +89,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", type=str, default=None, help="bm,bn,bk,depth for the GEMM (default: built-in)")
     ap.add_argument("--conv-tune", type=str, default=None, help="bm,bn,bk,depth for the conv (default: built-in)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed region, run one plain device copy of MIB MiB (a known-size kernel for "
+                         "scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -170,6 +173,16 @@ def main():
     log(f"conv {conv_ms.mean() * 1e3:.1f} us (median {np.median(conv_ms) * 1e3:.1f}) = {conv_tflops:.1f} TFLOP/s "
         f"({100 * conv_tflops / PEAK_BF16_TFLOPS:.1f}% of peak)")
     log(f"step {ms_per_step * 1e3:.1f} us -> {value:.1f} TFLOP/s; host wall {wall / args.steps * 1e3:.3f} ms/step")
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n * 4} bytes read and written once")
+        del src, dst
 
     base = None
     if not args.no_cpu_baseline:
