@@ -28,10 +28,11 @@ class IgcError(RuntimeError):
 
 
 class Tune(ctypes.Structure):
-    _fields_ = [("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int), ("pipe_depth", ctypes.c_int)]
+    _fields_ = [("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int), ("pipe_depth", ctypes.c_int),
+                ("waves", ctypes.c_int)]
 
     def astuple(self):
-        return (self.bm, self.bn, self.bk, self.pipe_depth)
+        return (self.bm, self.bn, self.bk, self.pipe_depth, self.waves)
 
 
 _lib = None
@@ -152,7 +153,7 @@ def igc_tune_lds_bytes(tune):
 
 
 def tunes():
-    """All compiled (bm, bn, bk, pipe_depth) configurations."""
+    """All compiled (bm, bn, bk, pipe_depth, waves) configurations."""
     return [igc_tune_get(i).astuple() for i in range(igc_tune_count())]
 
 

@@ -19,13 +19,15 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
+         "-I" + os.path.join(ROOT, "include"),
          # packed fp32 VALU ops are disabled for all device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def tile_configs():
     text = open(os.path.join(CSRC, "tile_configs.hpp")).read()
-    return [tuple(int(v) for v in m) for m in re.findall(r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", text)]
+    return [tuple(int(v) for v in m)
+            for m in re.findall(r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", text)]
 
 
 def _run(cmd):
@@ -39,9 +41,9 @@ def _run(cmd):
 def build(jobs=None, verbose=False):
     os.makedirs(OBJ_DIR, exist_ok=True)
     units = []
-    for (bm, bn, bk, d) in tile_configs():
-        obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}.o")
-        units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}",
+    for (bm, bn, bk, d, w) in tile_configs():
+        obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}.o")
+        units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}", f"-DIGC_W={w}",
                       "-c", os.path.join(CSRC, "instances.hip"), "-o", obj])
     for name in ("igc_lib", "registry"):
         units.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, name + ".hip"),

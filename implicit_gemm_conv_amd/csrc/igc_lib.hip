@@ -6,10 +6,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/igc.h"
+#include "igc.h"
 #include "instances.hpp"
 #include "mainloop.hpp"
 #include "ring.hpp"
+
+// Tiles of M that one XCD walks together (its share of the tile grid is
+// GROUP_M tiles tall): larger groups trade A-row reuse for B-column reuse in
+// that XCD's L2.
+#ifndef IGC_GROUP_M
+#define IGC_GROUP_M 8
+#endif
 
 namespace igc {
 
@@ -25,7 +32,7 @@ static const Instance* pick(const igc_tune_t* tune, bool fp16, bool a_kc, bool b
     } else {
         t = default_tune(M, N, K, conv);
     }
-    return find_instance(t.bm, t.bn, t.bk, t.pipe_depth, fp16, a_kc, b_kc, conv);
+    return find_instance(t, fp16, a_kc, b_kc, conv);
 }
 
 static igc_status_t launch(const Instance* inst, const Params& p, hipStream_t stream) {
@@ -35,7 +42,7 @@ static igc_status_t launch(const Instance* inst, const Params& p, hipStream_t st
     (void)hipGetLastError();  // launch errors below are ours alone
     Params arg = p;
     void* args[] = {&arg};
-    if (hipLaunchKernel(inst->fn, dim3((unsigned)grid), dim3(kThreads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(inst->fn, dim3((unsigned)grid), dim3(64 * inst->waves), args, 0, stream) != hipSuccess)
         return IGC_ERR_HIP;
     return hipGetLastError() == hipSuccess ? IGC_OK : IGC_ERR_HIP;
 }
@@ -80,6 +87,7 @@ static igc_status_t gemm_any(bool fp16, int64_t M, int64_t N, int64_t K, const v
     if ((M + inst->bm - 1) / inst->bm > 0x7fffffff || (N + inst->bn - 1) / inst->bn > 0x7fffffff)
         return IGC_ERR_UNSUPPORTED;
     p.out_kind = (int)ct;
+    p.group_m = IGC_GROUP_M;
     p.k_ragged8 = (K % 8) != 0;
     p.vec_ok = 1;
     return launch(inst, p, stream);
@@ -121,6 +129,7 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     p.tiles_n = (int)((Ng + inst->bn - 1) / inst->bn);
     if ((Mg + inst->bm - 1) / inst->bm > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
     p.out_kind = (int)yt;
+    p.group_m = IGC_GROUP_M;
     p.k_ragged8 = 0;  // C % 8 == 0
     p.vec_ok = (K % 8) == 0;  // NPQK rows are K elements: vector stores need 16-byte rows
     p.H = H;
@@ -192,7 +201,7 @@ igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int
 
 int igc_tune_supported(const igc_tune_t* tune) {
     if (!tune) return 0;
-    return find_instance(tune->bm, tune->bn, tune->bk, tune->pipe_depth, false, true, false, false) != nullptr;
+    return find_instance(*tune, false, true, false, false) != nullptr;
 }
 
 int igc_tune_count(void) { return num_tunes(); }
@@ -205,7 +214,7 @@ int igc_tune_get(int i, igc_tune_t* out) {
 
 int64_t igc_tune_lds_bytes(const igc_tune_t* tune) {
     if (!tune) return 0;
-    const Instance* inst = find_instance(tune->bm, tune->bn, tune->bk, tune->pipe_depth, false, true, false, false);
+    const Instance* inst = find_instance(*tune, false, true, false, false);
     return inst ? inst->lds_bytes : 0;
 }
 
@@ -243,7 +252,24 @@ int igc_ring_schedule(int D, int KT, int* ev, int cap) {
         ++n;
     };
     enum { ISSUE = 0, WAIT = 1, READ = 2, BARRIER = 3 };
-    if (D >= 2) {
+    if (Ring::spread(D)) {
+        const int KTp = (KT + D - 1) / D * D;
+        for (int s = 0; s + 1 < D; ++s) emit(ISSUE, s, Ring::slot(D, s));
+        emit(WAIT, 0, D - 2);
+        if (KTp > 0)
+            emit(READ, 0, Ring::slot(D, 0));
+        else
+            emit(BARRIER, 0, 0);  // K == 0: the kernel reads zeros it never uses
+        for (int t = 0; t < KTp; ++t) {
+            emit(ISSUE, t + D - 1, Ring::slot(D, t + D - 1));  // spread over tile t's k-steps
+            if (t + 1 < KTp) {
+                emit(WAIT, t + 1, D - 2);
+                emit(READ, t + 1, Ring::slot(D, t + 1));
+            } else {
+                emit(BARRIER, t, 0);
+            }
+        }
+    } else if (D >= 2) {
         // the K loop is padded to a multiple of D with zero-filled tiles
         const int KTp = (KT + D - 1) / D * D;
         for (int s = 0; s < D; ++s)

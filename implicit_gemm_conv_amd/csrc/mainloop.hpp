@@ -1,9 +1,9 @@
 // mainloop.hpp -- the software-pipelined bf16/fp16 MFMA mainloop for gfx950.
 //
-// One workgroup of 4 wave64s computes a BM x BN tile of C = A * B (or of the
-// implicit-GEMM view of an NHWC convolution).  Waves form a 2 x 2 grid; each
-// owns a (BM/2) x (BN/2) sub-tile held as 32x32 MFMA blocks of fp32
-// accumulators in registers for the whole K loop.
+// One workgroup of 4 or 8 wave64s computes a BM x BN tile of C = A * B (or of
+// the implicit-GEMM view of an NHWC convolution).  Waves form a 2 x (NW/2)
+// grid; each owns a sub-tile held as 32x32 MFMA blocks of fp32 accumulators in
+// registers for the whole K loop.
 //
 // Subsystems (the "B200 TMA Pipeline Designer" page, Executable steps 2-7,
 // re-done for CDNA4):
@@ -19,10 +19,10 @@
 //     applied on the global side (which 16-byte chunk each lane fetches) and
 //     undone by the fragment reader with the same map.  K-contiguous tiles
 //     (rows of BK elements) XOR the chunk index with (row&7)^((row>>3)&1)
-//     for BK = 64, or ((row>>1)^(row>>3))&3 for BK = 32;
+//     for BK = 64, or (row>>2)&3 for BK = 32;
 //     M/N-contiguous tiles (rows of BM or BN elements, read with the
 //     transposing ds_read_b64_tr_b16) XOR it with {0,6,12,10}[row&3].  Both make
-//     the 8- and 16-lane phases of a fragment read hit distinct banks.
+//     every lane phase of a fragment read hit distinct banks.
 //  3. MFMA loop: v_mfma_f32_32x32x16_{bf16,f16}; each lane holds 8 consecutive
 //     k of one row/column per operand.  B is passed as the first operand so
 //     that each lane's 4 consecutive accumulators are 4 consecutive output
@@ -67,8 +67,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kOob = 0x80000000u;          // buffer offset that is always out of range
 constexpr int kNumRecords = 0x7fffffff;         // range of every buffer resource
 constexpr int kRsrcFlags = 0x00020000;          // gfx9 raw buffer: 32-bit dword format
@@ -83,6 +81,7 @@ struct Params {
     int64_t lda, ldb, ldc;
     int tiles_m, tiles_n;
     int out_kind;
+    int group_m;     // tiles of M walked together inside one XCD's range (L2 reuse)
     int k_ragged8;   // K % 8 != 0: chunk straddling K must be zeroed
     int vec_ok;      // output rows allow 8/16-byte vector stores
     // convolution geometry (CONV instances only)
@@ -90,16 +89,18 @@ struct Params {
 };
 
 // XOR swizzle of the 16-byte chunk index within a K-contiguous LDS row of CPR
-// chunks.  A fragment read has 8 or 16 consecutive lanes on consecutive rows at
-// the same logical chunk; the map sends each such group to distinct 16-byte
-// bank groups, whether the LDS serves 128 or 256 bytes per cycle.
+// chunks.  On gfx950 the LDS serves a 128-bit read 16 lanes at a time over its
+// 64 banks (256 bytes); the 16 lanes of a phase are four lane quads of equal
+// quad parity, e.g. lanes {0-3, 12-15, 20-23, 24-27} (measured with the bank
+// conflict counter).  A fragment read puts lane l on row l%32 at one logical
+// chunk, so each phase must see 16 distinct (row, chunk) bank groups.
 template <int CPR>
 IGC_HD inline int swz_k(int row) {
     static_assert(CPR == 8 || CPR == 4, "K tile of 64 or 32 elements");
     if constexpr (CPR == 8) {
         return (row & 7) ^ ((row >> 3) & 1);  // 128-byte rows
     } else {
-        return ((row >> 1) ^ (row >> 3)) & 3;  // 64-byte rows, two per 128 bytes
+        return (row >> 2) & 3;  // 64-byte rows, four per 256 bytes
     }
 }
 // XOR swizzle of the 16-byte chunk index within an M/N-contiguous LDS row.
@@ -138,15 +139,15 @@ __device__ __forceinline__ f32x16_t mfma(i16x8_t a, i16x8_t b, f32x16_t c) {
 //   KC = true : LDS tile is ROWS rows of BK elements (K contiguous).
 //   KC = false: LDS tile is BK rows of ROWS elements (M or N contiguous).
 // ---------------------------------------------------------------------------
-template <int ROWS, int BK, bool KC>
+template <int ROWS, int BK, bool KC, int NW>
 struct Tile {
     static constexpr int BYTES = ROWS * BK * 2;
     static constexpr int INSTR = BYTES / 1024;        // 1 KB wave instructions per stage
-    static constexpr int IPW = INSTR / kWaves;        // per wave
+    static constexpr int IPW = INSTR / NW;            // per wave
     static constexpr int ROW_ELEMS = KC ? BK : ROWS;  // elements per LDS row
     static constexpr int CPR = ROW_ELEMS / 8;         // 16-byte chunks per LDS row
     static constexpr int RPI = 64 / CPR;              // LDS rows per wave instruction
-    static_assert(BYTES % (1024 * kWaves) == 0, "tile must split into whole wave instructions");
+    static_assert(BYTES % (1024 * NW) == 0, "tile must split into whole wave instructions");
     static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row must be 8..512 elements");
     // LDS row, physical chunk and logical chunk written by `lane` in wave instruction q.
     __device__ static int row_of(int q, int lane) { return q * RPI + lane / CPR; }
@@ -160,16 +161,27 @@ struct Tile {
     }
 };
 
-template <bool FP16_, int BM_, int BN_, int BK_, int D_, bool A_KC_, bool B_KC_, bool CONV_>
+template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, bool A_KC_, bool B_KC_, bool CONV_,
+          bool SPREAD_ = Ring::spread(D_)>
 struct Cfg {
     static constexpr bool FP16 = FP16_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, D = D_;
+    // NW wave64s in a 2 x (NW/2) grid.  With 8 waves two share each SIMD, so
+    // while one waits to issue a global->LDS load the other keeps the SIMD's
+    // matrix core busy.
+    static constexpr int NW = NW_, NT = 64 * NW_;
+    static constexpr int WM = 2, WN = NW_ / 2;
+    // SPREAD: the slot freed at the barrier before tile t is refilled (with tile
+    // t+D-1) by loads interleaved through tile t's k-steps, instead of one burst.
+    static constexpr bool SPREAD = SPREAD_;
     static constexpr bool A_KC = A_KC_, B_KC = B_KC_, CONV = CONV_;
-    static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave sub-tile
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-tile is whole 32x32 MFMA blocks");
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KK = BK / 16;                // MFMA k-steps per K tile
-    using TA = Tile<BM, BK, A_KC>;
-    using TB = Tile<BN, BK, B_KC>;
+    using TA = Tile<BM, BK, A_KC, NW>;
+    using TB = Tile<BN, BK, B_KC, NW>;
     static constexpr int STAGE_BYTES = TA::BYTES + TB::BYTES;
     static constexpr int LDS_BYTES = STAGE_BYTES * D;
     static constexpr int LPT = TA::IPW + TB::IPW;     // loads per K tile per wave
@@ -178,6 +190,8 @@ struct Cfg {
     static_assert(D >= 1 && D <= 8, "pipe depth");
     static_assert(LDS_BYTES <= 163840, "stage ring exceeds the 160 KB of LDS per CU");
     static_assert(D < 2 || (D - 2) * LPT < 64, "vmcnt cannot express that many loads in flight");
+    static_assert(!SPREAD || D >= 3, "refilling during compute needs a third slot");
+    static_assert(LPT % KK == 0, "loads must split evenly over the k-steps");
 };
 
 // Per-lane DMA state of one operand: offsets of the chunks this lane fetches
@@ -209,6 +223,8 @@ struct Mainloop {
     int conv_pix[C::CONV ? TA::IPW : 1];
     int conv_h0[C::CONV ? TA::IPW : 1];
     int conv_w0[C::CONV ? TA::IPW : 1];
+    // the swizzled K chunk this lane fetches (same for all its loads of an operand)
+    int ca_lane = 0, cb_lane = 0;
     // fragment read offsets (bytes within a stage's operand region)
     uint32_t fa_off[C::A_KC ? KK : FM];
     uint32_t fb_off[C::B_KC ? KK : FN];
@@ -216,19 +232,21 @@ struct Mainloop {
     __device__ __forceinline__ Mainloop(const Params p_, int64_t m0_, int64_t n0_) : p(p_), m0(m0_), n0(n0_) {
         lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        wm = wave >> 1;
-        wn = wave & 1;
+        wm = wave / C::WN;
+        wn = wave % C::WN;
         KT = (int)((p.K + BK - 1) / BK);
         KTp = (KT + D - 1) / D * D;
         setup_dma();
         setup_frag_offsets();
+        if constexpr (C::A_KC) ca_lane = TA::logical_chunk(wave, lane);
+        if constexpr (C::B_KC) cb_lane = TB::logical_chunk(wave, lane);
     }
 
     __device__ __forceinline__ void setup_dma() {
         // Operand A
 #pragma unroll
         for (int j = 0; j < TA::IPW; ++j) {
-            const int q = j * kWaves + wave;
+            const int q = j * C::NW + wave;
             const int row = TA::row_of(q, lane);
             const int c = TA::logical_chunk(q, lane);
             if constexpr (C::CONV) {
@@ -254,7 +272,7 @@ struct Mainloop {
         // Operand B
 #pragma unroll
         for (int j = 0; j < TB::IPW; ++j) {
-            const int q = j * kWaves + wave;
+            const int q = j * C::NW + wave;
             const int row = TB::row_of(q, lane);
             const int c = TB::logical_chunk(q, lane);
             if constexpr (C::B_KC) {
@@ -305,99 +323,95 @@ struct Mainloop {
         }
     }
 
-    // ---- global -> LDS: issue every load of K tile t into the given stage ----
-    // TAIL: t is the last K tile and K % BK != 0, so chunks past K are masked.
-    template <bool TAIL>
-    __device__ __forceinline__ void issue_tile(int t, IGC_LDS char* stage) {
+    // ---- global -> LDS: the loads of K tile t ---------------------------------
+    // Loads are numbered 0..LPT-1 (A's wave instructions, then B's).  Masking is
+    // branch-free: a chunk past M/N was given an out-of-range offset at setup; a
+    // chunk past K (the K tail, and every load of the padding tiles t >= KT) is
+    // masked per lane here.  Because q = j*4 + wave, a lane's swizzled K chunk is
+    // the same for all of its loads of one operand, so one compare per tile does.
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue_range(int t, IGC_LDS char* stage) {
         const int64_t k0 = (int64_t)t * BK;
-        constexpr bool tail = TAIL;
         IGC_LDS char* sa = stage;
         IGC_LDS char* sb = stage + TA::BYTES;
+        const int64_t krem = p.K - k0;  // valid K elements left from this tile on (may be <= 0)
         // ---- A
-        if constexpr (C::CONV) {
-            const char* xb = (const char*)p.A;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(xb);
-            const bool uniform_tap = (p.Cin % BK) == 0;
-            int r = 0, s = 0, cbase = 0;
-            if (uniform_tap) {
-                const int tap = (int)(k0 / p.Cin);
-                r = tap / p.S;
-                s = tap - r * p.S;
-                cbase = (int)(k0 - (int64_t)tap * p.Cin);
-            }
-#pragma unroll
-            for (int j = 0; j < TA::IPW; ++j) {
-                const int q = j * kWaves + wave;
-                const int c = TA::logical_chunk(q, lane);
-                int rr = r, ss = s, cin = cbase + 8 * c;
-                bool kok = !tail || k0 + 8 * c < p.K;
-                if (!uniform_tap) {
-                    const int kg = (int)k0 + 8 * c;
-                    kok = kok && kg < p.K;
-                    const int tap = kg / p.Cin;
-                    cin = kg - tap * p.Cin;
-                    rr = tap / p.S;
-                    ss = tap - rr * p.S;
+        if constexpr (J0 < TA::IPW) {
+            if constexpr (C::CONV) {
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A);
+                const bool uniform_tap = (p.Cin % BK) == 0;
+                int r = 0, s = 0, cbase = 0;
+                if (uniform_tap) {
+                    const int tap = (int)(k0 / p.Cin);
+                    r = tap / p.S;
+                    s = tap - r * p.S;
+                    cbase = (int)(k0 - (int64_t)tap * p.Cin);
                 }
-                const int h = conv_h0[j] + rr * p.dh;
-                const int w = conv_w0[j] + ss * p.dw;
-                const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
-                const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
-                dma16(rs, sa + q * 1024, ok ? off : kOob);
-            }
-        } else if constexpr (C::A_KC) {
-            const char* base = (const char*)p.A + (m0 * p.lda + k0) * 2;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-#pragma unroll
-            for (int j = 0; j < TA::IPW; ++j) {
-                const int q = j * kWaves + wave;
-                uint32_t off = da.voff[j];
-                if (tail && k0 + 8 * TA::logical_chunk(q, lane) >= p.K) off = kOob;
-                dma16(rs, sa + q * 1024, off);
-            }
-        } else {
-            const char* base = (const char*)p.A + (k0 * p.lda + m0) * 2;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-#pragma unroll
-            for (int j = 0; j < TA::IPW; ++j) {
-                const int q = j * kWaves + wave;
-                uint32_t off = da.voff[j];
-                if (tail && k0 + TA::row_of(q, lane) >= p.K) off = kOob;
-                dma16(rs, sa + q * 1024, off);
+                static_for<J0, (J1 < TA::IPW ? J1 : TA::IPW)>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = J;
+                    const int q = j * C::NW + wave;
+                    const int c = TA::logical_chunk(q, lane);
+                    int rr = r, ss = s, cin = cbase + 8 * c;
+                    bool kok = 8 * c < krem;
+                    if (!uniform_tap) {
+                        const int kg = (int)k0 + 8 * c;
+                        const int tap = kg / p.Cin;
+                        cin = kg - tap * p.Cin;
+                        rr = tap / p.S;
+                        ss = tap - rr * p.S;
+                    }
+                    const int h = conv_h0[j] + rr * p.dh;
+                    const int w = conv_w0[j] + ss * p.dw;
+                    const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+                    const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
+                    dma16(rs, sa + q * 1024, ok ? off : kOob);
+                });
+            } else if constexpr (C::A_KC) {
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (m0 * p.lda + k0) * 2);
+                const bool kout = 8 * ca_lane >= krem;
+                static_for<J0, (J1 < TA::IPW ? J1 : TA::IPW)>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = J;
+                    dma16(rs, sa + (j * C::NW + wave) * 1024, kout ? kOob : da.voff[j]);
+                });
+            } else {
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (k0 * p.lda + m0) * 2);
+                static_for<J0, (J1 < TA::IPW ? J1 : TA::IPW)>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = J;
+                    const int q = j * C::NW + wave;
+                    dma16(rs, sa + q * 1024, TA::row_of(q, lane) >= krem ? kOob : da.voff[j]);
+                });
             }
         }
         // ---- B
-        if constexpr (C::B_KC) {
-            const char* base = (const char*)p.B + (n0 * p.ldb + k0) * 2;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-#pragma unroll
-            for (int j = 0; j < TB::IPW; ++j) {
-                const int q = j * kWaves + wave;
-                uint32_t off = db.voff[j];
-                if (tail && k0 + 8 * TB::logical_chunk(q, lane) >= p.K) off = kOob;
-                dma16(rs, sb + q * 1024, off);
-            }
-        } else {
-            const char* base = (const char*)p.B + (k0 * p.ldb + n0) * 2;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-#pragma unroll
-            for (int j = 0; j < TB::IPW; ++j) {
-                const int q = j * kWaves + wave;
-                uint32_t off = db.voff[j];
-                if (tail && k0 + TB::row_of(q, lane) >= p.K) off = kOob;
-                dma16(rs, sb + q * 1024, off);
+        if constexpr (J1 > TA::IPW) {
+            constexpr int B0 = J0 > TA::IPW ? J0 - TA::IPW : 0;
+            constexpr int B1 = J1 - TA::IPW;
+            if constexpr (C::B_KC) {
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (n0 * p.ldb + k0) * 2);
+                const bool kout = 8 * cb_lane >= krem;
+                static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = J;
+                    dma16(rs, sb + (j * C::NW + wave) * 1024, kout ? kOob : db.voff[j]);
+                });
+            } else {
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (k0 * p.ldb + n0) * 2);
+                static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = J;
+                    const int q = j * C::NW + wave;
+                    dma16(rs, sb + q * 1024, TB::row_of(q, lane) >= krem ? kOob : db.voff[j]);
+                });
             }
         }
     }
 
-    // Tiles t >= KT are phantom tiles (the K loop is rounded up to a multiple
-    // of the ring depth): every one of their loads is out of bounds, so the
-    // slot fills with zeros and the MFMAs on it add exact zeros.
-    __device__ __forceinline__ void issue(int t, IGC_LDS char* stage) {
-        if ((int64_t)(t + 1) * BK > p.K)
-            issue_tile<true>(t, stage);
-        else
-            issue_tile<false>(t, stage);
+    // All loads of tile t.  Tiles t >= KT are padding tiles: every load is out
+    // of range, the slot fills with zeros and the MFMAs on it add exact zeros.
+    __device__ __forceinline__ void issue(int t, IGC_LDS char* stage) { issue_range<0, C::LPT>(t, stage); }
+
+    // Part PART of NPARTS of the loads of tile t.
+    template <int PART, int NPARTS>
+    __device__ __forceinline__ void issue_part(int t, IGC_LDS char* stage) {
+        issue_range<PART * C::LPT / NPARTS, (PART + 1) * C::LPT / NPARTS>(t, stage);
     }
 
     // After this wave's loads of K tile t have landed and before the barrier:
@@ -429,50 +443,53 @@ struct Mainloop {
         if constexpr (C::A_KC && !C::CONV) {
 #pragma unroll
             for (int j = 0; j < TA::IPW; ++j) {
-                const int q = j * kWaves + wave;
+                const int q = j * C::NW + wave;
                 fix(stage, q, TA::logical_chunk(q, lane));
             }
         }
         if constexpr (C::B_KC) {
 #pragma unroll
             for (int j = 0; j < TB::IPW; ++j) {
-                const int q = j * kWaves + wave;
+                const int q = j * C::NW + wave;
                 fix(stage + TA::BYTES, q, TB::logical_chunk(q, lane));
             }
         }
     }
 
     // ---- LDS -> registers: fragments of one MFMA k-step ----------------------
+    // Order: A fragment 0, every B fragment, then the other A fragments -- the
+    // order in which the MFMAs of the k-step consume them.
+    __device__ __forceinline__ void read_a(const IGC_LDS char* sa, int kk, int i, i16x8_t& f) {
+        if constexpr (C::A_KC) {
+            f = *(const IGC_LDS i16x8_t*)(sa + fa_off[kk] + i * 32 * BK * 2);
+        } else {
+            const IGC_LDS char* a0 = sa + fa_off[i] + (16 * kk) * BM * 2;
+            i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)a0);
+            i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(a0 + 4 * BM * 2));
+            f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
+    __device__ __forceinline__ void read_b(const IGC_LDS char* sb, int kk, int j, i16x8_t& f) {
+        if constexpr (C::B_KC) {
+            f = *(const IGC_LDS i16x8_t*)(sb + fb_off[kk] + j * 32 * BK * 2);
+        } else {
+            const IGC_LDS char* b0 = sb + fb_off[j] + (16 * kk) * BN * 2;
+            i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)b0);
+            i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(b0 + 4 * BN * 2));
+            f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
     __device__ __forceinline__ void read_frags(const IGC_LDS char* stage, int kk, i16x8_t (&fa)[FM], i16x8_t (&fb)[FN]) {
         const IGC_LDS char* sa = stage;
         const IGC_LDS char* sb = stage + TA::BYTES;
-        if constexpr (C::A_KC) {
+        read_a(sa, kk, 0, fa[0]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *(const IGC_LDS i16x8_t*)(sa + fa_off[kk] + i * 32 * BK * 2);
-        } else {
+        for (int j = 0; j < FN; ++j) read_b(sb, kk, j, fb[j]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const IGC_LDS char* a0 = sa + fa_off[i] + (16 * kk) * BM * 2;
-                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)a0);
-                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(a0 + 4 * BM * 2));
-                fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-        }
-        if constexpr (C::B_KC) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *(const IGC_LDS i16x8_t*)(sb + fb_off[kk] + j * 32 * BK * 2);
-        } else {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const IGC_LDS char* b0 = sb + fb_off[j] + (16 * kk) * BN * 2;
-                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)b0);
-                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(b0 + 4 * BN * 2));
-                fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-        }
+        for (int i = 1; i < FM; ++i) read_a(sa, kk, i, fa[i]);
     }
+    // LDS read instructions of one k-step
+    static constexpr int DS_READS = FM * (C::A_KC ? 1 : 2) + FN * (C::B_KC ? 1 : 2);
 
     __device__ __forceinline__ static void mma(f32x16_t (&acc)[FM][FN], const i16x8_t (&fa)[FM], const i16x8_t (&fb)[FN]) {
 #pragma unroll
@@ -567,8 +584,8 @@ __device__ __forceinline__ void ring_barrier() {
 // each XCD has its own L2: give every XCD a contiguous range of tile ids, and
 // walk that range GROUP_M tiles down M at a time so the tiles resident on one
 // XCD share A rows and B columns in its L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-    constexpr int kXcds = 8, kGroupM = 4;
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int kGroupM, int& tm, int& tn) {
+    constexpr int kXcds = 8;
     const int G = tiles_m * tiles_n;
     const int wg = blockIdx.x;
     const int q = G / kXcds, r = G % kXcds, x = wg % kXcds, i = wg / kXcds;
@@ -582,6 +599,22 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
     tn = in / gm;
 }
 
+// Scheduling template for one k-step region: NM MFMAs with ND LDS reads and
+// NV global->LDS loads spread between them, so the reads and loads issue while
+// earlier MFMAs execute instead of in a burst ahead of them.
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave() {
+    constexpr int kMfma = 0x008, kDsRead = 0x100, kVmemRead = 0x020;
+    static_for<0, NM>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = I;
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        constexpr int d0 = i * ND / NM, d1 = (i + 1) * ND / NM;
+        if constexpr (d1 > d0) __builtin_amdgcn_sched_group_barrier(kDsRead, d1 - d0, 0);
+        constexpr int v0 = i * NV / NM, v1 = (i + 1) * NV / NM;
+        if constexpr (v1 > v0) __builtin_amdgcn_sched_group_barrier(kVmemRead, v1 - v0, 0);
+    });
+}
+
 // LDS slot U of the stage ring of configuration C: one __shared__ array per
 // slot, so every slot is a distinct object to the compiler.
 template <class C, int U>
@@ -591,12 +624,12 @@ __device__ __forceinline__ IGC_LDS char* stage() {
 }
 
 template <class C>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
+__global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     using ML = Mainloop<C>;
     constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN;
 
     int tm, tn;
-    tile_coords(p.tiles_m, p.tiles_n, tm, tn);
+    tile_coords(p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN);
     const int KT = ml.KT, KTp = ml.KTp;
 
@@ -609,7 +642,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
 
     // The accumulators are never updated under a branch: every K tile of the
     // padded loop runs the same MFMA sequence, so no copies of them are needed.
-    if constexpr (D >= 2) {
+    constexpr int NMF = FM * FN;
+    constexpr int DSR = ML::DS_READS;
+    if constexpr (D >= 2 && C::SPREAD) {
+        // ---- prologue: tiles 0 .. D-2; slot D-1 is refilled during tile 0
+        static_for<0, D - 1>([&](auto S) __attribute__((always_inline)) { ml.issue(S, stage<C, S>()); });
+        ml.template wait_tiles<D - 2>(D - 2);
+        ml.fixup_ragged_k(0, stage<C, 0>());
+        ring_barrier();
+        ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+        for (int t0 = 0; t0 < KTp; t0 += D) {
+            static_for<0, D>([&](auto U) __attribute__((always_inline)) {
+                constexpr int u = U;
+                constexpr int un = (u + 1) % D;
+                constexpr int uf = (u + D - 1) % D;  // slot of tile t-1, freed by the last barrier
+                const int t = t0 + u;
+                // k-steps 0 .. KK-2: refill slot uf with tile t+D-1, read ahead, MFMA
+                static_for<0, KK - 1>([&](auto KS) __attribute__((always_inline)) {
+                    constexpr int kk = KS;
+                    ml.template issue_part<kk, KK>(t + D - 1, stage<C, uf>());
+                    ml.read_frags(stage<C, u>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                    ML::mma(acc, fa[kk & 1], fb[kk & 1]);
+                    interleave<NMF, DSR, C::LPT / KK>();
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                ml.template issue_part<KK - 1, KK>(t + D - 1, stage<C, uf>());
+                // ready(t+1) and free(t): D-2 newer tiles may stay in flight
+                ml.template wait_tiles<D - 2>(D - 2);
+                ml.fixup_ragged_k(t + 1, stage<C, un>());
+                ring_barrier();
+                ml.read_frags(stage<C, un>(), 0, fa[0], fb[0]);
+                ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+                interleave<NMF, DSR, 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        wait_vmcnt<0>();  // the padding tiles past the loop are still landing in free slots
+    } else if constexpr (D >= 2) {
         // ---- prologue: fill the ring
         static_for<0, D>([&](auto S) __attribute__((always_inline)) {
             if (S < KTp) ml.issue(S, stage<C, S>());
@@ -628,6 +697,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Params p) {
                     constexpr int kk = KS;
                     ml.read_frags(stage<C, u>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                     ML::mma(acc, fa[kk & 1], fb[kk & 1]);
+                    interleave<NMF, DSR, 0>();
                     __builtin_amdgcn_sched_barrier(0);  // k-steps stay in order: two fragment sets live
                 });
                 // ready(t+1): own loads landed, then everyone; free(t): all reads of t done.

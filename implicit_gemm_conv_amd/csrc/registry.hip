@@ -4,14 +4,14 @@
 namespace igc {
 
 static const igc_tune_t kTunes[] = {
-#define IGC_TUNE_ENTRY(BM, BN, BK, D) {BM, BN, BK, D},
+#define IGC_TUNE_ENTRY(BM, BN, BK, D, W) {BM, BN, BK, D, W},
     IGC_FOR_EACH_TILE(IGC_TUNE_ENTRY)
 #undef IGC_TUNE_ENTRY
 };
 
 typedef const Instance* (*TableFn)(int*);
 static const TableFn kTables[] = {
-#define IGC_TABLE_ENTRY(BM, BN, BK, D) &instance_table_##BM##x##BN##x##BK##x##D,
+#define IGC_TABLE_ENTRY(BM, BN, BK, D, W) &instance_table_##BM##x##BN##x##BK##x##D##x##W,
     IGC_FOR_EACH_TILE(IGC_TABLE_ENTRY)
 #undef IGC_TABLE_ENTRY
 };
@@ -20,14 +20,14 @@ int num_tunes() { return (int)(sizeof(kTunes) / sizeof(kTunes[0])); }
 
 igc_tune_t tune_at(int i) { return kTunes[i]; }
 
-const Instance* find_instance(int bm, int bn, int bk, int d, bool fp16, bool a_kc, bool b_kc, bool conv) {
+const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_kc, bool conv) {
     for (TableFn fn : kTables) {
         int n = 0;
         const Instance* t = fn(&n);
         for (int i = 0; i < n; ++i) {
             const Instance& e = t[i];
-            if (e.bm == bm && e.bn == bn && e.bk == bk && e.d == d && e.fp16 == fp16 && e.a_kc == a_kc &&
-                e.b_kc == b_kc && e.conv == conv)
+            if (e.bm == q.bm && e.bn == q.bn && e.bk == q.bk && e.d == q.pipe_depth && e.waves == q.waves &&
+                e.fp16 == fp16 && e.a_kc == a_kc && e.b_kc == b_kc && e.conv == conv)
                 return &e;
         }
     }
@@ -39,7 +39,7 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
     (void)N;
     (void)K;
     (void)conv;
-    return igc_tune_t{256, 256, 64, 2};
+    return igc_tune_t{256, 256, 32, 4, 8};
 }
 
 }  // namespace igc

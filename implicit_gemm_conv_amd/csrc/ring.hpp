@@ -24,9 +24,17 @@
 //              compute the last k-step of t (operands already in registers)
 //   epilogue : nothing left in flight; accumulators go to the output.
 //
+// D >= 3 ("spread" rings): the prologue issues tiles 0 .. D-2 only; after the
+// barrier before tile t, the slot of tile t-1 is free and is refilled with tile
+// t+D-1 by loads interleaved through tile t's k-steps.  Every wait then allows
+// exactly D-2 newer tiles in flight.
+//
 // D == 1 has a single slot, so the next tile can only be issued after the
 // barrier that frees it, and must be waited for at once (no overlap); it is
 // kept as the no-pipelining baseline.
+//
+// In both pipelined forms the K loop is padded to a multiple of D with tiles
+// whose loads are all out of range (they land as zeros).
 #pragma once
 
 #if defined(__HIPCC__)
@@ -48,6 +56,10 @@ struct Ring {
         return issued_before_wait(D, KT, t) - 1 - t;
     }
     IGC_HD static constexpr int slot(int D, int tile) { return tile % D; }
+    // Rings of three or more stages refill the slot freed at a barrier during
+    // the next tile's k-steps (loads interleaved with the MFMAs); two-stage
+    // rings issue the refill right after the barrier.
+    IGC_HD static constexpr bool spread(int D) { return D >= 3; }
     IGC_HD static constexpr int prologue_tiles(int D, int KT) { return D < KT ? D : KT; }
 };
 

@@ -53,11 +53,12 @@ typedef enum { IGC_ROW_MAJOR = 0, IGC_COL_MAJOR = 1 } igc_layout_t;
 
 typedef enum { IGC_OUT_F32 = 0, IGC_OUT_BF16 = 1, IGC_OUT_F16 = 2 } igc_out_t;
 
-/* Optional tuning: output tile BM x BN, K tile BK, and PIPE_DEPTH = number of
- * LDS stages in the ring.  Only compiled combinations are accepted (see
+/* Optional tuning: output tile BM x BN, K tile BK, PIPE_DEPTH = number of LDS
+ * stages in the ring, and the number of wave64s per workgroup (4: one per SIMD;
+ * 8: two per SIMD).  Only compiled combinations are accepted (see
  * igc_tune_supported); NULL selects the built-in choice for the shape. */
 typedef struct {
-    int bm, bn, bk, pipe_depth;
+    int bm, bn, bk, pipe_depth, waves;
 } igc_tune_t;
 
 /*
@@ -118,7 +119,7 @@ igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int
                                           const void *x, const void *w, void *y, igc_out_t y_type, int fp16,
                                           const igc_tune_t *tune, igc_stream_t stream);
 
-/* 1 if (bm, bn, bk, pipe_depth) is a compiled configuration, else 0. */
+/* 1 if (bm, bn, bk, pipe_depth, waves) is a compiled configuration, else 0. */
 int igc_tune_supported(const igc_tune_t *tune);
 
 /* Number of compiled configurations; igc_tune_get(i, &t) fills t for i in [0, count). */
@@ -145,7 +146,11 @@ const char *igc_status_string(igc_status_t status);
  *            every schedule ends with one once nothing is left in flight).
  * For pipe_depth >= 2 the K loop is padded to a multiple of pipe_depth with
  * tiles whose loads are all out of range (they land as zeros and add nothing),
- * so tiles up to that padded count appear.  Each wave drains its own LDS reads
+ * so tiles up to that padded count appear.  For pipe_depth >= 3 the prologue
+ * issues pipe_depth-1 tiles and, during each tile t, the loads of tile
+ * t+pipe_depth-1 are issued (interleaved with t's MFMAs) into the slot the last
+ * barrier freed; tiles past the padded count are issued out of range and never
+ * read.  Each wave drains its own LDS reads
  * before every barrier, so a barrier after a tile's reads frees its slot.
  * Returns the number of events (which may exceed cap), or -1 on bad input.
  * This is the exact sequence the kernels execute.
