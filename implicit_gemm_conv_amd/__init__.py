@@ -29,9 +29,10 @@ class IgcError(RuntimeError):
 
 class Tune(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int), ("pipe_depth", ctypes.c_int),
-                ("waves", ctypes.c_int)]
+                ("waves", ctypes.c_int), ("k_splits", ctypes.c_int)]
 
     def astuple(self):
+        """(bm, bn, bk, pipe_depth, waves): the compiled configuration."""
         return (self.bm, self.bn, self.bk, self.pipe_depth, self.waves)
 
 
@@ -59,6 +60,8 @@ def lib():
             fn.restype = i32
         L.igc_tune_supported.argtypes = [ctypes.POINTER(Tune)]
         L.igc_tune_supported.restype = i32
+        L.igc_default_tune.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Tune)]
+        L.igc_default_tune.restype = i32
         L.igc_tune_count.argtypes = []
         L.igc_tune_count.restype = i32
         L.igc_tune_get.argtypes = [i32, ctypes.POINTER(Tune)]
@@ -137,6 +140,14 @@ def conv2d_nhwc_implicit_gemm_ex(N, H, W, C, K, R, S, stride_h, stride_w, pad_h,
 
 def igc_tune_supported(tune):
     return lib().igc_tune_supported(_tune(tune))
+
+
+def igc_default_tune(M, N, K, conv=0):
+    """The Tune the library picks for an M x N x K problem (conv: implicit-GEMM view)."""
+    t = Tune()
+    if not lib().igc_default_tune(M, N, K, int(conv), ctypes.byref(t)):
+        raise ValueError("bad shape")
+    return t
 
 
 def igc_tune_count():

@@ -45,7 +45,7 @@ def build(jobs=None, verbose=False):
         obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}.o")
         units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}", f"-DIGC_W={w}",
                       "-c", os.path.join(CSRC, "instances.hip"), "-o", obj])
-    for name in ("igc_lib", "registry"):
+    for name in ("igc_lib", "registry", "split_reduce"):
         units.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, name + ".hip"),
                       "-o", os.path.join(OBJ_DIR, name + ".o")])
     jobs = jobs or min(len(units), max(1, (os.cpu_count() or 4)))

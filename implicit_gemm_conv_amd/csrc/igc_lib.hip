@@ -10,6 +10,7 @@
 #include "instances.hpp"
 #include "mainloop.hpp"
 #include "ring.hpp"
+#include "split_reduce.hpp"
 
 // Tiles of M that one XCD walks together (its share of the tile grid is
 // GROUP_M tiles tall): larger groups trade A-row reuse for B-column reuse in
@@ -24,26 +25,57 @@ static bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr
 
 static int out_size(igc_out_t t) { return t == IGC_OUT_F32 ? 4 : 2; }
 
-static const Instance* pick(const igc_tune_t* tune, bool fp16, bool a_kc, bool b_kc, bool conv, int64_t M,
-                            int64_t N, int64_t K) {
-    igc_tune_t t;
-    if (tune) {
-        t = *tune;
-    } else {
-        t = default_tune(M, N, K, conv);
-    }
-    return find_instance(t, fp16, a_kc, b_kc, conv);
+struct Plan {
+    const Instance* inst = nullptr;
+    int splits = 1;
+};
+
+// The tile configuration and K split for one call: an explicit tune is taken as
+// is (k_splits <= 1: no split); otherwise the built-in choice for the shape.
+static Plan pick(const igc_tune_t* tune, bool fp16, bool a_kc, bool b_kc, bool conv, int64_t M, int64_t N,
+                 int64_t K) {
+    const igc_tune_t t = tune ? *tune : default_tune(M, N, K, conv);
+    Plan pl;
+    pl.inst = find_instance(t, fp16, a_kc, b_kc, conv);
+    pl.splits = t.k_splits > 1 ? t.k_splits : 1;
+    return pl;
 }
 
-static igc_status_t launch(const Instance* inst, const Params& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    if (grid <= 0) return IGC_OK;
-    if (grid > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+// Launches the mainloop (and, for a K split, the fixed-order reduction).  With
+// S > 1 splits the fp32 partial tiles live in a stream-ordered workspace taken
+// with hipMallocAsync and released with hipFreeAsync after the reduction is
+// enqueued, so concurrent calls on different streams never share it.
+static igc_status_t launch(const Plan& pl, Params p, hipStream_t stream) {
+    const Instance* inst = pl.inst;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles <= 0) return IGC_OK;
+    int S = 1;
+    p.k_per_split = p.K > 0 ? p.K : 1;
+    if (pl.splits > 1 && p.K > 0) {
+        // each split a whole number of rings: K per split rounded up to BK * PIPE_DEPTH
+        const int64_t unit = (int64_t)inst->bk * inst->d;
+        const int64_t per = ((p.K + pl.splits - 1) / pl.splits + unit - 1) / unit * unit;
+        S = (int)((p.K + per - 1) / per);
+        p.k_per_split = per;
+    }
+    if (tiles * S > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+    p.k_splits = S;
     (void)hipGetLastError();  // launch errors below are ours alone
+    float* ws = nullptr;
+    if (S > 1) {
+        p.ldws = (p.N + 3) / 4 * 4;
+        p.ws_stride = p.M * p.ldws;
+        if (hipMallocAsync((void**)&ws, (size_t)(S * p.ws_stride) * sizeof(float), stream) != hipSuccess)
+            return IGC_ERR_HIP;
+        p.ws = ws;
+    }
     Params arg = p;
     void* args[] = {&arg};
-    if (hipLaunchKernel(inst->fn, dim3((unsigned)grid), dim3(64 * inst->waves), args, 0, stream) != hipSuccess)
-        return IGC_ERR_HIP;
+    hipError_t e = hipLaunchKernel(inst->fn, dim3((unsigned)(tiles * S)), dim3(64 * inst->waves), args, 0, stream);
+    if (e == hipSuccess && S > 1)
+        e = launch_split_reduce(ws, S, p.ws_stride, p.M, p.N, p.ldws, p.C, p.ldc, p.out_kind, stream);
+    if (ws) (void)hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return IGC_ERR_HIP;
     return hipGetLastError() == hipSuccess ? IGC_OK : IGC_ERR_HIP;
 }
 
@@ -55,7 +87,8 @@ static igc_status_t gemm_any(bool fp16, int64_t M, int64_t N, int64_t K, const v
         return IGC_ERR_INVALID_VALUE;
     if (ct != IGC_OUT_F32 && ct != IGC_OUT_BF16 && ct != IGC_OUT_F16) return IGC_ERR_INVALID_VALUE;
     const bool a_kc = la == IGC_ROW_MAJOR, b_kc = lb == IGC_COL_MAJOR;
-    const Instance* inst = pick(tune, fp16, a_kc, b_kc, false, M, N, K);
+    const Plan pl = pick(tune, fp16, a_kc, b_kc, false, M, N, K);
+    const Instance* inst = pl.inst;
     if (!inst) return IGC_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return IGC_OK;
     if (!C || ldc < N) return IGC_ERR_INVALID_VALUE;
@@ -90,7 +123,7 @@ static igc_status_t gemm_any(bool fp16, int64_t M, int64_t N, int64_t K, const v
     p.group_m = IGC_GROUP_M;
     p.k_ragged8 = (K % 8) != 0;
     p.vec_ok = 1;
-    return launch(inst, p, stream);
+    return launch(pl, p, stream);
 }
 
 static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R, int S, int sh, int sw, int ph,
@@ -105,7 +138,8 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     if (hspan < 0 || wspan < 0) return IGC_ERR_INVALID_VALUE;
     const int64_t P = hspan / sh + 1, Q = wspan / sw + 1;
     const int64_t Mg = (int64_t)N * P * Q, Ng = K, Kg = (int64_t)R * S * C;
-    const Instance* inst = pick(tune, fp16, true, true, true, Mg, Ng, Kg);
+    const Plan pl = pick(tune, fp16, true, true, true, Mg, Ng, Kg);
+    const Instance* inst = pl.inst;
     if (!inst) return IGC_ERR_UNSUPPORTED;
     if (Mg == 0 || Ng == 0) return IGC_OK;
     if (!x || !w || !y) return IGC_ERR_INVALID_VALUE;
@@ -145,7 +179,7 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     p.pw = pw;
     p.dh = dh;
     p.dw = dw;
-    return launch(inst, p, stream);
+    return launch(pl, p, stream);
 }
 
 }  // namespace igc
@@ -202,6 +236,12 @@ igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int
 int igc_tune_supported(const igc_tune_t* tune) {
     if (!tune) return 0;
     return find_instance(*tune, false, true, false, false) != nullptr;
+}
+
+int igc_default_tune(int64_t M, int64_t N, int64_t K, int conv, igc_tune_t* out) {
+    if (!out || M < 0 || N < 0 || K < 0) return 0;
+    *out = default_tune(M, N, K, conv != 0);
+    return 1;
 }
 
 int igc_tune_count(void) { return num_tunes(); }

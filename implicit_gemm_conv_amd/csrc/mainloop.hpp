@@ -82,6 +82,13 @@ struct Params {
     int tiles_m, tiles_n;
     int out_kind;
     int group_m;     // tiles of M walked together inside one XCD's range (L2 reuse)
+    // split-K: k_splits workgroups share each output tile, split s covering
+    // K in [s*k_per_split, min(K, (s+1)*k_per_split)); each writes its fp32
+    // partial tile to ws + s*ws_stride (row pitch ldws) instead of C.
+    int k_splits;
+    int64_t k_per_split;
+    float* ws;
+    int64_t ldws, ws_stride;
     int k_ragged8;   // K % 8 != 0: chunk straddling K must be zeroed
     int vec_ok;      // output rows allow 8/16-byte vector stores
     // convolution geometry (CONV instances only)
@@ -215,6 +222,7 @@ struct Mainloop {
     const Params p;  // a copy: kernel arguments stay in scalar registers
     int lane, wave, wm, wn;
     int64_t m0, n0;  // tile origin
+    int64_t kbase, kend;  // this workgroup's K range
     int KT;          // number of K tiles
     int KTp;         // KT rounded up to a multiple of D (phantom tiles load zeros)
     DmaState<TA::IPW> da;
@@ -229,12 +237,13 @@ struct Mainloop {
     uint32_t fa_off[C::A_KC ? KK : FM];
     uint32_t fb_off[C::B_KC ? KK : FN];
 
-    __device__ __forceinline__ Mainloop(const Params p_, int64_t m0_, int64_t n0_) : p(p_), m0(m0_), n0(n0_) {
+    __device__ __forceinline__ Mainloop(const Params p_, int64_t m0_, int64_t n0_, int64_t kbase_, int64_t kend_)
+        : p(p_), m0(m0_), n0(n0_), kbase(kbase_), kend(kend_) {
         lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         wm = wave / C::WN;
         wn = wave % C::WN;
-        KT = (int)((p.K + BK - 1) / BK);
+        KT = (int)((kend - kbase + BK - 1) / BK);
         KTp = (KT + D - 1) / D * D;
         setup_dma();
         setup_frag_offsets();
@@ -331,10 +340,10 @@ struct Mainloop {
     // the same for all of its loads of one operand, so one compare per tile does.
     template <int J0, int J1>
     __device__ __forceinline__ void issue_range(int t, IGC_LDS char* stage) {
-        const int64_t k0 = (int64_t)t * BK;
+        const int64_t k0 = kbase + (int64_t)t * BK;
         IGC_LDS char* sa = stage;
         IGC_LDS char* sb = stage + TA::BYTES;
-        const int64_t krem = p.K - k0;  // valid K elements left from this tile on (may be <= 0)
+        const int64_t krem = kend - k0;  // valid K elements left from this tile on (may be <= 0)
         // ---- A
         if constexpr (J0 < TA::IPW) {
             if constexpr (C::CONV) {
@@ -418,7 +427,7 @@ struct Mainloop {
     // when K % 8 != 0, the chunk straddling K holds elements k >= K read from
     // beyond the row's end; the lane that fetched it zeroes them.
     __device__ __forceinline__ void fixup_ragged_k(int t, IGC_LDS char* stage) {
-        const int64_t k0 = (int64_t)t * BK;
+        const int64_t k0 = kbase + (int64_t)t * BK;
         if (!p.k_ragged8 || k0 + BK <= p.K) return;
         // the only chunk that straddles K is the one starting at k0 + 8*cs
         const int cs = (int)((p.K - k0) >> 3);
@@ -515,8 +524,9 @@ struct Mainloop {
     }
 
     // ---- epilogue: accumulators -> C ---------------------------------------
-    __device__ __forceinline__ void store(const f32x16_t (&acc)[FM][FN]) {
-        const bool full = p.vec_ok && (m0 + BM <= p.M) && (n0 + BN <= p.N);
+    __device__ __forceinline__ void store(const f32x16_t (&acc)[FM][FN], void* dst, int64_t ldc, int kind,
+                                          bool vec_ok) {
+        const bool full = vec_ok && (m0 + BM <= p.M) && (n0 + BN <= p.N);
         const int64_t mrow = m0 + wm * C::WTM + (lane & 31);
         const int64_t ncol = n0 + wn * C::WTN + 4 * (lane >> 5);
 #pragma unroll
@@ -531,16 +541,16 @@ struct Mainloop {
                     const int64_t n = ncol + 32 * j + 8 * g;
                     const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
                     const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                    const int64_t off = m * p.ldc + n;
+                    const int64_t off = m * ldc + n;
                     if (full) {
-                        if (p.out_kind == OUT_F32) {
-                            *(f32x4_t*)((float*)p.C + off) = f32x4_t{v0, v1, v2, v3};
-                        } else if (p.out_kind == OUT_BF16) {
+                        if (kind == OUT_F32) {
+                            *(f32x4_t*)((float*)dst + off) = f32x4_t{v0, v1, v2, v3};
+                        } else if (kind == OUT_BF16) {
                             typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-                            *(bf16x4_t*)((__bf16*)p.C + off) = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                            *(bf16x4_t*)((__bf16*)dst + off) = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
                         } else {
                             typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
-                            *(f16x4_t*)((_Float16*)p.C + off) =
+                            *(f16x4_t*)((_Float16*)dst + off) =
                                 f16x4_t{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
                         }
                     } else if (m < p.M) {
@@ -548,12 +558,12 @@ struct Mainloop {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             if (n + e < p.N) {
-                                if (p.out_kind == OUT_F32)
-                                    ((float*)p.C)[off + e] = v[e];
-                                else if (p.out_kind == OUT_BF16)
-                                    ((__bf16*)p.C)[off + e] = (__bf16)v[e];
+                                if (kind == OUT_F32)
+                                    ((float*)dst)[off + e] = v[e];
+                                else if (kind == OUT_BF16)
+                                    ((__bf16*)dst)[off + e] = (__bf16)v[e];
                                 else
-                                    ((_Float16*)p.C)[off + e] = (_Float16)v[e];
+                                    ((_Float16*)dst)[off + e] = (_Float16)v[e];
                             }
                         }
                     }
@@ -584,10 +594,9 @@ __device__ __forceinline__ void ring_barrier() {
 // each XCD has its own L2: give every XCD a contiguous range of tile ids, and
 // walk that range GROUP_M tiles down M at a time so the tiles resident on one
 // XCD share A rows and B columns in its L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int kGroupM, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int kGroupM, int& tm, int& tn) {
     constexpr int kXcds = 8;
     const int G = tiles_m * tiles_n;
-    const int wg = blockIdx.x;
     const int q = G / kXcds, r = G % kXcds, x = wg % kXcds, i = wg / kXcds;
     const int id = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
     const int group = kGroupM * tiles_n;
@@ -628,9 +637,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     using ML = Mainloop<C>;
     constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN;
 
+    // workgroups s*T .. s*T+T-1 (T output tiles) take K split s
+    const int T = p.tiles_m * p.tiles_n;
+    const int split = (int)blockIdx.x / T;
     int tm, tn;
-    tile_coords(p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN);
+    tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int64_t kbase = (int64_t)split * p.k_per_split;
+    const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
+    ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN, kbase, kend);
     const int KT = ml.KT, KTp = ml.KTp;
 
     f32x16_t acc[FM][FN];
@@ -736,7 +750,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
         }
     }
     // ---- output epilogue: nothing is in flight any more
-    ml.store(acc);
+    if (p.k_splits > 1)
+        ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
+    else
+        ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
 }
 
 }  // namespace igc

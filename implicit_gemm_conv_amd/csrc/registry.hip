@@ -4,7 +4,7 @@
 namespace igc {
 
 static const igc_tune_t kTunes[] = {
-#define IGC_TUNE_ENTRY(BM, BN, BK, D, W) {BM, BN, BK, D, W},
+#define IGC_TUNE_ENTRY(BM, BN, BK, D, W) {BM, BN, BK, D, W, 0},
     IGC_FOR_EACH_TILE(IGC_TUNE_ENTRY)
 #undef IGC_TUNE_ENTRY
 };
@@ -35,11 +35,23 @@ const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_
 }
 
 igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
-    (void)M;
-    (void)N;
-    (void)K;
     (void)conv;
-    return igc_tune_t{256, 256, 32, 4, 8};
+    constexpr int64_t kCUs = 256;
+    // Enough 256x256 tiles for every CU: the largest tile (least global and LDS
+    // traffic per flop), 8 waves, a 4-stage ring of 32-deep K tiles.
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 >= kCUs) return igc_tune_t{256, 256, 32, 4, 8, 1};
+    // Otherwise 128x128 tiles, and split K until every CU has a workgroup
+    // (each split keeps at least 2048 of K).
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    int64_t S = 1;
+    if (t128 > 0 && t128 < kCUs) {
+        S = (kCUs + t128 - 1) / t128;
+        if (S > K / 2048) S = K / 2048;
+        if (S > 16) S = 16;
+        if (S < 1) S = 1;
+    }
+    return igc_tune_t{128, 128, 64, 4, 4, (int)S};
 }
 
 }  // namespace igc

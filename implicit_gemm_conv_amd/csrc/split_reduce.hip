@@ -1,0 +1,48 @@
+// split_reduce.hip -- second pass of split-K: C = sum over splits of the fp32
+// partial tiles, added in split order 0, 1, ..., S-1 (fixed, so results are
+// bit-reproducible), then rounded once to the output type.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "split_reduce.hpp"
+
+namespace igc {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4r_t;
+
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws, int S, int64_t ws_stride,
+                                                           int64_t M, int64_t N, int64_t ldws, void* C,
+                                                           int64_t ldc, int kind) {
+    const int64_t n4 = (N + 3) / 4;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= M * n4) return;
+    const int64_t m = idx / n4;
+    const int64_t n = (idx - m * n4) * 4;
+    // ldws is a multiple of 4 and >= N rounded up to 4: the 16-byte read stays in the row
+    const float* src = ws + m * ldws + n;
+    f32x4r_t acc = *(const f32x4r_t*)src;
+    for (int s = 1; s < S; ++s) acc += *(const f32x4r_t*)(src + s * ws_stride);
+    for (int e = 0; e < 4; ++e) {
+        if (n + e >= N) break;
+        const int64_t off = m * ldc + n + e;
+        if (kind == 0)
+            ((float*)C)[off] = acc[e];
+        else if (kind == 1)
+            ((__bf16*)C)[off] = (__bf16)acc[e];
+        else
+            ((_Float16*)C)[off] = (_Float16)acc[e];
+    }
+}
+
+hipError_t launch_split_reduce(const float* ws, int S, int64_t ws_stride, int64_t M, int64_t N, int64_t ldws,
+                               void* C, int64_t ldc, int kind, hipStream_t stream) {
+    const int64_t work = M * ((N + 3) / 4);
+    if (work <= 0) return hipSuccess;
+    const int64_t blocks = (work + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, S, ws_stride, M, N,
+                       ldws, C, ldc, kind);
+    return hipGetLastError();
+}
+
+}  // namespace igc

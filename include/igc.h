@@ -15,8 +15,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *   never allocates, frees or retains them and keeps no per-call state; calls
- *   are thread-safe.
+ *   never frees or retains them and keeps no per-call state; calls are
+ *   thread-safe.  A call that splits K takes a temporary fp32 workspace
+ *   (k_splits * M * N * 4 bytes, N rounded up to 4) with hipMallocAsync on
+ *   `stream` and releases it with hipFreeAsync on the same stream; no other
+ *   call allocates.
  * - Each call only validates its arguments and enqueues work on `stream`
  *   (a hipStream_t; NULL = the default stream).  It returns before the GPU
  *   finishes; synchronise the stream to observe the result.
@@ -54,11 +57,15 @@ typedef enum { IGC_ROW_MAJOR = 0, IGC_COL_MAJOR = 1 } igc_layout_t;
 typedef enum { IGC_OUT_F32 = 0, IGC_OUT_BF16 = 1, IGC_OUT_F16 = 2 } igc_out_t;
 
 /* Optional tuning: output tile BM x BN, K tile BK, PIPE_DEPTH = number of LDS
- * stages in the ring, and the number of wave64s per workgroup (4: one per SIMD;
- * 8: two per SIMD).  Only compiled combinations are accepted (see
- * igc_tune_supported); NULL selects the built-in choice for the shape. */
+ * stages in the ring, the number of wave64s per workgroup (4: one per SIMD;
+ * 8: two per SIMD), and k_splits (<= 1: none; S > 1: split K into up to S
+ * ranges computed by separate workgroups whose fp32 partial tiles are summed
+ * in split order by a second kernel).  Only compiled (bm, bn, bk, pipe_depth,
+ * waves) combinations are accepted (see igc_tune_supported); NULL selects the
+ * built-in choice for the shape (which splits K when the output has too few
+ * tiles to occupy every CU). */
 typedef struct {
-    int bm, bn, bk, pipe_depth, waves;
+    int bm, bn, bk, pipe_depth, waves, k_splits;
 } igc_tune_t;
 
 /*
@@ -121,6 +128,10 @@ igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int
 
 /* 1 if (bm, bn, bk, pipe_depth, waves) is a compiled configuration, else 0. */
 int igc_tune_supported(const igc_tune_t *tune);
+
+/* The configuration the library picks for an M x N x K problem (conv != 0: the
+ * implicit-GEMM view of a convolution) when no tune is given; 1 on success. */
+int igc_default_tune(int64_t M, int64_t N, int64_t K, int conv, igc_tune_t *out);
 
 /* Number of compiled configurations; igc_tune_get(i, &t) fills t for i in [0, count). */
 int igc_tune_count(void);

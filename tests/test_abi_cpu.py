@@ -108,6 +108,20 @@ def test_tune_table_fits_lds():
     assert igc.igc_tune_supported((256, 256, 64, 2, 6)) == 0
 
 
+@pytest.mark.parametrize("shape,expect", [
+    ((8192, 8192, 8192), ((256, 256, 32, 4, 8), 1)),      # enough 256x256 tiles for 256 CUs: no split
+    ((100352, 256, 2304), ((256, 256, 32, 4, 8), 1)),     # the 3x3 conv's GEMM view
+    ((2048, 1024, 16384), ((128, 128, 64, 4, 4), 2)),     # 128 tiles of 128x128: split K in two
+    ((1000, 1000, 65536), ((128, 128, 64, 4, 4), 4)),     # 64 tiles: four splits
+    ((128, 96, 200), ((128, 128, 64, 4, 4), 1)),          # too little K to split
+    ((0, 5, 7), ((128, 128, 64, 4, 4), 1)),
+])
+def test_default_tune(shape, expect):
+    t = igc.igc_default_tune(*shape)
+    assert (t.astuple(), t.k_splits) == expect
+    assert igc.igc_tune_supported(t) == 1
+
+
 ISSUE, WAIT, READ, BARRIER = 0, 1, 2, 3
 
 

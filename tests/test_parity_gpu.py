@@ -192,6 +192,38 @@ def test_k_chain_tags(tune):
         assert np.all(y == float(tags.sum())), f"k-chain tune={tune} K={K}: {np.unique(y)[:5]}"
 
 
+@pytest.mark.parametrize("tune", [(128, 128, 64, 4, 4), (256, 256, 32, 4, 8), (256, 128, 64, 3, 4)])
+def test_split_k(tune):
+    """K split over 2..8 workgroups per tile, fp32 partials summed in split order: ragged K, every layout."""
+    cases = [(300, 270, 1000, "row", "row", 2, "f32", "bf16"), (257, 129, 777, "row", "col", 3, "bf16", "bf16"),
+             (130, 200, 4096, "col", "row", 5, "f16", "fp16"), (64, 72, 200, "col", "col", 8, "f32", "bf16"),
+             (1000, 1000, 6144, "row", "row", 4, "f32", "fp16")]
+    for (M, N, K, la, lb, S, out, dtype) in cases:
+        say(f"split-K tune {tune} S={S} {M}x{N}x{K} {la}/{lb} {dtype}->{out}")
+        gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=300 + S, tune=tuple(tune) + (S,))
+
+
+def test_split_k_deterministic_and_exact():
+    """Integer inputs: every split's partial and the fixed-order sum are exact, so the result equals the
+    oracle bit for bit and repeats bit for bit."""
+    M, N, K = 384, 256, 3000
+    A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", 3000, 256, "bf16", ("int", 4), ("int", 4), seed=8)
+    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=(128, 128, 64, 4, 4, 6))[0]
+            for _ in range(2)]
+    ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row")
+    assert np.array_equal(outs[0], ref) and np.array_equal(outs[0], outs[1])
+
+
+def test_conv_split_k():
+    N, H, W, C, K = 2, 7, 7, 256, 64
+    x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=41)
+    for S in (2, 3):
+        say(f"conv split-K S={S}")
+        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=(128, 128, 64, 4, 4, S))
+        ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
+        assert_close(y, ref, Sabs, "bf16", f"conv split {S}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 def test_exact_integers_bit_exact(dtype, out):
