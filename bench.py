@@ -87,8 +87,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tune", type=str, default=None, help="bm,bn,bk,depth for the GEMM (default: built-in)")
-    ap.add_argument("--conv-tune", type=str, default=None, help="bm,bn,bk,depth for the conv (default: built-in)")
+    ap.add_argument("--tune", type=str, default=None, help="bm,bn,bk,depth,waves,mfma,half_stage[,k_splits] for the GEMM (default: built-in)")
+    ap.add_argument("--conv-tune", type=str, default=None, help="bm,bn,bk,depth,waves,mfma,half_stage[,k_splits] for the conv (default: built-in)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run one plain device copy of MIB MiB (a known-size kernel for "
                          "scaling hardware byte counters)")

@@ -29,11 +29,12 @@ class IgcError(RuntimeError):
 
 class Tune(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int), ("pipe_depth", ctypes.c_int),
-                ("waves", ctypes.c_int), ("k_splits", ctypes.c_int)]
+                ("waves", ctypes.c_int), ("mfma", ctypes.c_int), ("half_stage", ctypes.c_int),
+                ("k_splits", ctypes.c_int)]
 
     def astuple(self):
-        """(bm, bn, bk, pipe_depth, waves): the compiled configuration."""
-        return (self.bm, self.bn, self.bk, self.pipe_depth, self.waves)
+        """(bm, bn, bk, pipe_depth, waves, mfma, half_stage): the compiled configuration."""
+        return (self.bm, self.bn, self.bk, self.pipe_depth, self.waves, self.mfma or 32, self.half_stage)
 
 
 _lib = None
@@ -70,7 +71,7 @@ def lib():
         L.igc_tune_lds_bytes.restype = i64
         L.igc_status_string.argtypes = [i32]
         L.igc_status_string.restype = ctypes.c_char_p
-        L.igc_ring_schedule.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int), i32]
+        L.igc_ring_schedule.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_int), i32]
         L.igc_ring_schedule.restype = i32
         _lib = L
     return _lib
@@ -164,7 +165,7 @@ def igc_tune_lds_bytes(tune):
 
 
 def tunes():
-    """All compiled (bm, bn, bk, pipe_depth, waves) configurations."""
+    """All compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage) configurations."""
     return [igc_tune_get(i).astuple() for i in range(igc_tune_count())]
 
 
@@ -175,14 +176,14 @@ def igc_status_string(status):
 status_string = igc_status_string
 
 
-def igc_ring_schedule(pipe_depth, k_tiles):
-    """The mainloop's event list [(kind, tile, slot_or_inflight), ...] (see include/igc.h)."""
-    n = lib().igc_ring_schedule(pipe_depth, k_tiles, None, 0)
+def igc_ring_schedule(pipe_depth, k_tiles, half_stage=0):
+    """The mainloop's event list [(kind, tile, operand, x), ...] (see include/igc.h)."""
+    n = lib().igc_ring_schedule(pipe_depth, half_stage, k_tiles, None, 0)
     if n < 0:
         raise ValueError("bad ring parameters")
-    buf = (ctypes.c_int * (3 * max(n, 1)))()
-    lib().igc_ring_schedule(pipe_depth, k_tiles, buf, n)
-    return [(buf[3 * i], buf[3 * i + 1], buf[3 * i + 2]) for i in range(n)]
+    buf = (ctypes.c_int * (4 * max(n, 1)))()
+    lib().igc_ring_schedule(pipe_depth, half_stage, k_tiles, buf, n)
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
 
 
 def check(status):

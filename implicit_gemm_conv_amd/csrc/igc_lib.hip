@@ -52,8 +52,8 @@ static igc_status_t launch(const Plan& pl, Params p, hipStream_t stream) {
     int S = 1;
     p.k_per_split = p.K > 0 ? p.K : 1;
     if (pl.splits > 1 && p.K > 0) {
-        // each split a whole number of rings: K per split rounded up to BK * PIPE_DEPTH
-        const int64_t unit = (int64_t)inst->bk * inst->d;
+        // each split a whole number of ring periods (no padding tiles inside a split)
+        const int64_t unit = (int64_t)inst->bk * Ring::period(Ring::units(inst->d, inst->half));
         const int64_t per = ((p.K + pl.splits - 1) / pl.splits + unit - 1) / unit * unit;
         S = (int)((p.K + per - 1) / per);
         p.k_per_split = per;
@@ -280,67 +280,84 @@ int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chu
     return logical_chunk ^ swz_mn(row);
 }
 
-int igc_ring_schedule(int D, int KT, int* ev, int cap) {
-    if (D < 1 || D > 8 || KT < 0 || cap < 0 || (cap > 0 && !ev)) return -1;
+int igc_ring_schedule(int D, int half, int KT, int* ev, int cap) {
+    if (D < 1 || D > 8 || half < 0 || half > 1 || (half && D < 2) || KT < 0 || cap < 0 || (cap > 0 && !ev))
+        return -1;
+    const int U = Ring::units(D, half);
     int n = 0;
-    auto emit = [&](int kind, int tile, int slot) {
+    auto emit = [&](int kind, int tile, int op, int x) {
         if (n < cap) {
-            ev[3 * n] = kind;
-            ev[3 * n + 1] = tile;
-            ev[3 * n + 2] = slot;
+            ev[4 * n] = kind;
+            ev[4 * n + 1] = tile;
+            ev[4 * n + 2] = op;
+            ev[4 * n + 3] = x;
         }
         ++n;
     };
     enum { ISSUE = 0, WAIT = 1, READ = 2, BARRIER = 3 };
-    if (Ring::spread(D)) {
-        const int KTp = (KT + D - 1) / D * D;
-        for (int s = 0; s + 1 < D; ++s) emit(ISSUE, s, Ring::slot(D, s));
-        emit(WAIT, 0, D - 2);
+    auto issue_unit = [&](int s) { emit(ISSUE, s / 2, s % 2, Ring::slot_of(U, s)); };
+    auto read_tile = [&](int t) {
+        emit(READ, t, 0, Ring::slot_of(U, 2 * t));
+        emit(READ, t, 1, Ring::slot_of(U, 2 * t + 1));
+    };
+    // the K loop is padded to whole ring periods with zero-filled tiles
+    const int P = Ring::period(U);
+    const int KTp = (KT + P - 1) / P * P;
+    if (Ring::spread(U)) {
+        for (int s = 0; s < U - 2; ++s) issue_unit(s);
+        emit(WAIT, 0, -1, Ring::wait_units(U));
         if (KTp > 0)
-            emit(READ, 0, Ring::slot(D, 0));
+            read_tile(0);
         else
-            emit(BARRIER, 0, 0);  // K == 0: the kernel reads zeros it never uses
+            emit(BARRIER, 0, -1, 0);  // K == 0: the kernel reads zeros it never uses
         for (int t = 0; t < KTp; ++t) {
-            emit(ISSUE, t + D - 1, Ring::slot(D, t + D - 1));  // spread over tile t's k-steps
+            issue_unit(2 * t + U - 2);  // both spread over tile t's k-steps
+            issue_unit(2 * t + U - 1);
             if (t + 1 < KTp) {
-                emit(WAIT, t + 1, D - 2);
-                emit(READ, t + 1, Ring::slot(D, t + 1));
+                emit(WAIT, t + 1, -1, Ring::wait_units(U));
+                read_tile(t + 1);
             } else {
-                emit(BARRIER, t, 0);
+                emit(BARRIER, t, -1, 0);
             }
         }
     } else if (D >= 2) {
-        // the K loop is padded to a multiple of D with zero-filled tiles
-        const int KTp = (KT + D - 1) / D * D;
-        for (int s = 0; s < D; ++s)
-            if (s < KTp) emit(ISSUE, s, Ring::slot(D, s));
+        for (int t = 0; t < D; ++t)
+            if (t < KTp) {
+                issue_unit(2 * t);
+                issue_unit(2 * t + 1);
+            }
         if (KTp > 0) {
-            emit(WAIT, 0, Ring::inflight_after(D, KTp, 0));
-            emit(READ, 0, Ring::slot(D, 0));
+            emit(WAIT, 0, -1, 2 * Ring::inflight_after(D, KTp, 0));
+            read_tile(0);
         }
         for (int t = 0; t < KTp; ++t) {
             if (t + 1 < KTp) {
-                emit(WAIT, t + 1, Ring::inflight_after(D, KTp, t + 1));
-                if (t + D < KTp) emit(ISSUE, t + D, Ring::slot(D, t + D));
-                emit(READ, t + 1, Ring::slot(D, t + 1));
+                emit(WAIT, t + 1, -1, 2 * Ring::inflight_after(D, KTp, t + 1));
+                if (t + D < KTp) {
+                    issue_unit(2 * (t + D));
+                    issue_unit(2 * (t + D) + 1);
+                }
+                read_tile(t + 1);
             } else {
-                emit(BARRIER, t, 0);  // drained; the kernel's trailing read is of no tile
+                emit(BARRIER, t, -1, 0);  // drained; the kernel's trailing read is of no tile
             }
         }
     } else {
         if (KT > 0) {
-            emit(ISSUE, 0, 0);
-            emit(WAIT, 0, 0);
-            emit(READ, 0, 0);
+            issue_unit(0);
+            issue_unit(1);
+            emit(WAIT, 0, -1, 0);
+            read_tile(0);
         }
         for (int t = 0; t < KT; ++t) {
-            emit(BARRIER, t, 0);
+            emit(BARRIER, t, -1, 0);
             if (t + 1 < KT) {
-                emit(ISSUE, t + 1, 0);
-                emit(WAIT, t + 1, 0);
-                emit(READ, t + 1, 0);
+                issue_unit(2 * (t + 1));
+                issue_unit(2 * (t + 1) + 1);
+                emit(WAIT, t + 1, -1, 0);
+                read_tile(t + 1);
             } else {
-                emit(BARRIER, t, 0);
+                emit(BARRIER, t, -1, 0);
             }
         }
     }

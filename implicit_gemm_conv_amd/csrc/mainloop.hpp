@@ -2,8 +2,8 @@
 //
 // One workgroup of 4 or 8 wave64s computes a BM x BN tile of C = A * B (or of
 // the implicit-GEMM view of an NHWC convolution).  Waves form a 2 x (NW/2)
-// grid; each owns a sub-tile held as 32x32 MFMA blocks of fp32 accumulators in
-// registers for the whole K loop.
+// grid; each owns a sub-tile held as MI x MI MFMA blocks (MI = 32 or 16) of
+// fp32 accumulators in registers for the whole K loop.
 //
 // Subsystems (the "B200 TMA Pipeline Designer" page, Executable steps 2-7,
 // re-done for CDNA4):
@@ -18,15 +18,18 @@
 //  2. Swizzle: the direct-to-LDS destination is fixed, so the XOR swizzle is
 //     applied on the global side (which 16-byte chunk each lane fetches) and
 //     undone by the fragment reader with the same map.  K-contiguous tiles
-//     (rows of BK elements) XOR the chunk index with (row&7)^((row>>3)&1)
-//     for BK = 64, or (row>>2)&3 for BK = 32;
-//     M/N-contiguous tiles (rows of BM or BN elements, read with the
-//     transposing ds_read_b64_tr_b16) XOR it with {0,6,12,10}[row&3].  Both make
-//     every lane phase of a fragment read hit distinct banks.
-//  3. MFMA loop: v_mfma_f32_32x32x16_{bf16,f16}; each lane holds 8 consecutive
-//     k of one row/column per operand.  B is passed as the first operand so
-//     that each lane's 4 consecutive accumulators are 4 consecutive output
-//     columns (vector stores in the epilogue).
+//     (rows of BK elements) XOR the chunk index with (row>>1)&7 for BK = 64,
+//     or (-(row>>2))&3 for BK = 32; M/N-contiguous tiles (rows of BM or BN
+//     elements, read with the transposing ds_read_b64_tr_b16) XOR it with
+//     4*(row&3) + 2*((row>>3)&1).  Each map makes every lane phase of a
+//     fragment read hit distinct banks for both MFMA shapes.
+//  3. MFMA loop: v_mfma_f32_32x32x16 or v_mfma_f32_16x16x32, {bf16,f16}; each
+//     lane holds 8 consecutive k of one row/column per operand.  B is passed
+//     as the first operand so that each lane's 4 consecutive accumulators are
+//     4 consecutive output columns (vector stores in the epilogue).  Both
+//     shapes run at the same rate per clock, but the 16x16x32 form rewrites
+//     its accumulators half as often per flop (K = 32 per instruction), and
+//     under sustained load it holds a markedly higher clock on gfx950.
 //  4. Boundary: rows/columns past M/N and k past K load as zeros; when K is not
 //     a multiple of 8 the lane that loaded a chunk straddling K zeroes its tail
 //     in LDS after its own wait and before the barrier.  The epilogue stores
@@ -38,6 +41,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ring.hpp"
 
@@ -99,19 +104,24 @@ struct Params {
 // chunks.  On gfx950 the LDS serves a 128-bit read 16 lanes at a time over its
 // 64 banks (256 bytes); the 16 lanes of a phase are four lane quads of equal
 // quad parity, e.g. lanes {0-3, 12-15, 20-23, 24-27} (measured with the bank
-// conflict counter).  A fragment read puts lane l on row l%32 at one logical
-// chunk, so each phase must see 16 distinct (row, chunk) bank groups.
+// conflict counter).  A 32x32x16 fragment read puts lane l on row l%32 at
+// logical chunk 2kk + l/32, a 16x16x32 one on row l%16 at chunk 4kk + l/16;
+// both must give each phase 16 distinct (row, chunk) bank groups.  The maps
+// depend on row % 16 only, so every 16-row fragment sees the same pattern.
 template <int CPR>
 IGC_HD inline int swz_k(int row) {
     static_assert(CPR == 8 || CPR == 4, "K tile of 64 or 32 elements");
     if constexpr (CPR == 8) {
-        return (row & 7) ^ ((row >> 3) & 1);  // 128-byte rows
+        return (row >> 1) & 7;  // 128-byte rows
     } else {
-        return (row >> 2) & 3;  // 64-byte rows, four per 256 bytes
+        return (-(row >> 2)) & 3;  // 64-byte rows, four per 256 bytes
     }
 }
-// XOR swizzle of the 16-byte chunk index within an M/N-contiguous LDS row.
-IGC_HD inline int swz_mn(int row) { return (0xAC60 >> ((row & 3) * 4)) & 0xF; }  // {0,6,12,10}
+// XOR swizzle of the 16-byte chunk index within an M/N-contiguous LDS row (at
+// least 16 chunks).  ds_read_b64_tr_b16 serves 32 lanes per phase; a 32x32x16
+// fragment read covers 4 k-rows x 4 chunks per phase, a 16x16x32 one 8 k-rows
+// (r and r+8, r = 0..3) x 2 chunks.
+IGC_HD inline int swz_mn(int row) { return 4 * (row & 3) + 2 * ((row >> 3) & 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords, kRsrcFlags);
@@ -129,7 +139,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }  // lgkmcnt(0) only
 
-// MFMA 32x32x16, fp32 accumulate.
+// MFMA 32x32x16 (16 accumulators per lane) or 16x16x32 (4 per lane), fp32
+// accumulate; the accumulator type selects the shape.
 template <bool FP16>
 __device__ __forceinline__ f32x16_t mfma(i16x8_t a, i16x8_t b, f32x16_t c) {
     if constexpr (FP16) {
@@ -137,6 +148,16 @@ __device__ __forceinline__ f32x16_t mfma(i16x8_t a, i16x8_t b, f32x16_t c) {
                                                       c, 0, 0, 0);
     } else {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+template <bool FP16>
+__device__ __forceinline__ f32x4_t mfma(i16x8_t a, i16x8_t b, f32x4_t c) {
+    if constexpr (FP16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
 }
@@ -168,36 +189,60 @@ struct Tile {
     }
 };
 
-template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, bool A_KC_, bool B_KC_, bool CONV_,
-          bool SPREAD_ = Ring::spread(D_)>
+template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, int MI_, int HALF_, bool A_KC_, bool B_KC_,
+          bool CONV_>
 struct Cfg {
     static constexpr bool FP16 = FP16_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, D = D_;
+    // The ring holds U = 2*D + HALF operand slots: A(t) is unit 2t and B(t)
+    // unit 2t+1 of a sequence whose unit s lives in slot s % U (ring.hpp).
+    static constexpr int HALF = HALF_;
+    static constexpr int U = 2 * D_ + HALF_;
+    // MFMA block edge: 32 (32x32x16) or 16 (16x16x32)
+    static constexpr int MI = MI_;
+    static_assert(MI == 32 || MI == 16, "32x32x16 or 16x16x32 MFMA");
+    static constexpr int KS = MI == 32 ? 16 : 32;     // K depth of one MFMA (one k-step)
+    static constexpr int NH = 64 / MI;                // lane groups per fragment: 16-byte chunks per k-step
+    using Acc = typename std::conditional<MI == 32, f32x16_t, f32x4_t>::type;
     // NW wave64s in a 2 x (NW/2) grid.  With 8 waves two share each SIMD, so
     // while one waits to issue a global->LDS load the other keeps the SIMD's
     // matrix core busy.
     static constexpr int NW = NW_, NT = 64 * NW_;
     static constexpr int WM = 2, WN = NW_ / 2;
-    // SPREAD: the slot freed at the barrier before tile t is refilled (with tile
-    // t+D-1) by loads interleaved through tile t's k-steps, instead of one burst.
-    static constexpr bool SPREAD = SPREAD_;
+    // SPREAD: the two operand slots freed at the barrier before tile t are
+    // refilled by loads interleaved through tile t's k-steps, instead of one
+    // burst after the barrier.
+    static constexpr bool SPREAD = Ring::spread(U);
     static constexpr bool A_KC = A_KC_, B_KC = B_KC_, CONV = CONV_;
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave sub-tile is whole 32x32 MFMA blocks");
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KK = BK / 16;                // MFMA k-steps per K tile
+    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave sub-tile is whole MFMA blocks");
+    static constexpr int FM = WTM / MI, FN = WTN / MI;
+    static constexpr int KK = BK / KS;                // MFMA k-steps per K tile
+    static_assert(KK >= 1 && BK % KS == 0, "K tile is whole k-steps");
     using TA = Tile<BM, BK, A_KC, NW>;
     using TB = Tile<BN, BK, B_KC, NW>;
-    static constexpr int STAGE_BYTES = TA::BYTES + TB::BYTES;
-    static constexpr int LDS_BYTES = STAGE_BYTES * D;
+    // Slot s holds A units when s is even and U is even, B units when s is
+    // odd and U is even; with U odd both operands rotate through every slot.
+    static constexpr int SLOT_A = TA::BYTES, SLOT_B = TB::BYTES;
+    static constexpr int SLOT_MAX = SLOT_A > SLOT_B ? SLOT_A : SLOT_B;
+    template <int S>
+    static constexpr int slot_bytes() { return U % 2 ? SLOT_MAX : (S % 2 ? SLOT_B : SLOT_A); }
+    static constexpr int LDS_BYTES = U % 2 ? U * SLOT_MAX : D * (SLOT_A + SLOT_B);
     static constexpr int LPT = TA::IPW + TB::IPW;     // loads per K tile per wave
+    // the slot pattern repeats every P tiles; the K loop is unrolled by P
+    static constexpr int P = Ring::period(U);
     static_assert(!CONV || A_KC, "im2col operand is channel (K) contiguous");
-    static_assert(KK % 2 == 0, "fragment double-buffer parity needs an even number of k-steps");
+    static_assert(HALF == 0 || HALF == 1, "at most one extra operand slot");
+    static_assert(HALF == 0 || D >= 2, "an odd ring needs at least five operand slots");
+    // fragments alternate between two register sets by k-step, so one period
+    // of the unrolled loop must hold an even number of k-steps
+    static_assert((P * KK) % 2 == 0, "fragment double-buffer parity needs an even number of k-steps per period");
     static_assert(D >= 1 && D <= 8, "pipe depth");
     static_assert(LDS_BYTES <= 163840, "stage ring exceeds the 160 KB of LDS per CU");
-    static_assert(D < 2 || (D - 2) * LPT < 64, "vmcnt cannot express that many loads in flight");
-    static_assert(!SPREAD || D >= 3, "refilling during compute needs a third slot");
+    static_assert(!SPREAD || Ring::wait_units(U) * (TA::IPW > TB::IPW ? TA::IPW : TB::IPW) < 64,
+                  "vmcnt cannot express that many loads in flight");
+    static_assert(SPREAD || HALF == 0, "odd rings are refilled during compute");
     static_assert(LPT % KK == 0, "loads must split evenly over the k-steps");
 };
 
@@ -216,7 +261,8 @@ struct Mainloop {
     using TA = typename C::TA;
     using TB = typename C::TB;
     static constexpr int BM = C::BM, BN = C::BN, BK = C::BK, D = C::D, KK = C::KK;
-    static constexpr int FM = C::FM, FN = C::FN;
+    static constexpr int FM = C::FM, FN = C::FN, MI = C::MI, KS = C::KS, NH = C::NH;
+    using Acc = typename C::Acc;
 
     // ---- per-workgroup setup -------------------------------------------------
     const Params p;  // a copy: kernel arguments stay in scalar registers
@@ -224,7 +270,7 @@ struct Mainloop {
     int64_t m0, n0;  // tile origin
     int64_t kbase, kend;  // this workgroup's K range
     int KT;          // number of K tiles
-    int KTp;         // KT rounded up to a multiple of D (phantom tiles load zeros)
+    int KTp;         // KT rounded up to a multiple of the ring period (padding tiles load zeros)
     DmaState<TA::IPW> da;
     DmaState<TB::IPW> db;
     // im2col: per A instruction, the pixel base offset and top-left input coordinate
@@ -244,7 +290,7 @@ struct Mainloop {
         wm = wave / C::WN;
         wn = wave % C::WN;
         KT = (int)((kend - kbase + BK - 1) / BK);
-        KTp = (KT + D - 1) / D * D;
+        KTp = (KT + C::P - 1) / C::P * C::P;
         setup_dma();
         setup_frag_offsets();
         if constexpr (C::A_KC) ca_lane = TA::logical_chunk(wave, lane);
@@ -297,55 +343,64 @@ struct Mainloop {
     }
 
     __device__ __forceinline__ void setup_frag_offsets() {
+        // K-contiguous: lane reads row (wave row + MI*i + lane%MI), logical chunk
+        // NH*kk + lane/MI (the lane's 8 k of the k-step).  The swizzle depends on
+        // row % 16 only, so it is the same for every fragment i.
+        // M/N-contiguous (ds_read_b64_tr_b16, 4 k-rows x 16 columns per 16-lane
+        // group g, lane i16 addressing k-row i16/4 and columns 4*(i16%4)..+3):
+        //   32x32x16: group g covers k-rows 8*(g/2).. of the k-step and the
+        //             16 columns 16*(g%2).. of a 32-column fragment;
+        //   16x16x32: group g covers k-rows 8*g.. and the fragment's 16 columns.
+        // The k-row's swizzle depends on bits 0, 1 and 3 of the row only, which
+        // the k-step origin and the +4-row second read leave unchanged.
+        const int g = lane >> 4, i16 = lane & 15;
+        const int mn_rowpart = MI == 32 ? 8 * (g >> 1) + (i16 >> 2) : 8 * g + (i16 >> 2);
+        const int mn_u = MI == 32 ? 2 * (g & 1) + ((i16 & 3) >> 1) : ((i16 & 3) >> 1);
+        const int mn_s = swz_mn(mn_rowpart);
         if constexpr (C::A_KC) {
-            // lane reads row (wm*WTM + 32i + lane%32), logical chunk 2*kk + lane/32
-            const int row = wm * C::WTM + (lane & 31);
-            const int x = (lane >> 5) ^ swz_k<TA::CPR>(row);
+            const int row = wm * C::WTM + (lane % MI);
+            const int x = (lane / MI) ^ swz_k<TA::CPR>(row);
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fa_off[kk] = row * BK * 2 + (((2 * kk) ^ x) * 16);
+            for (int kk = 0; kk < KK; ++kk) fa_off[kk] = row * BK * 2 + (((NH * kk) ^ x) * 16);
         } else {
-            const int g = lane >> 4, i16 = lane & 15;
-            const int rowpart = 8 * (g >> 1) + (i16 >> 2);
-            const int u = 2 * (g & 1) + ((i16 & 3) >> 1);
-            const int s = swz_mn(i16 >> 2);
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int cl = (wm * C::WTM) / 8 + 4 * i + u;
-                fa_off[i] = rowpart * BM * 2 + ((cl ^ s) * 16) + 8 * (i16 & 1);
+                const int cl = (wm * C::WTM) / 8 + (MI / 8) * i + mn_u;
+                fa_off[i] = mn_rowpart * BM * 2 + ((cl ^ mn_s) * 16) + 8 * (i16 & 1);
             }
         }
         if constexpr (C::B_KC) {
-            const int row = wn * C::WTN + (lane & 31);
-            const int x = (lane >> 5) ^ swz_k<TB::CPR>(row);
+            const int row = wn * C::WTN + (lane % MI);
+            const int x = (lane / MI) ^ swz_k<TB::CPR>(row);
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) fb_off[kk] = row * BK * 2 + (((2 * kk) ^ x) * 16);
+            for (int kk = 0; kk < KK; ++kk) fb_off[kk] = row * BK * 2 + (((NH * kk) ^ x) * 16);
         } else {
-            const int g = lane >> 4, i16 = lane & 15;
-            const int rowpart = 8 * (g >> 1) + (i16 >> 2);
-            const int u = 2 * (g & 1) + ((i16 & 3) >> 1);
-            const int s = swz_mn(i16 >> 2);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int cl = (wn * C::WTN) / 8 + 4 * j + u;
-                fb_off[j] = rowpart * BN * 2 + ((cl ^ s) * 16) + 8 * (i16 & 1);
+                const int cl = (wn * C::WTN) / 8 + (MI / 8) * j + mn_u;
+                fb_off[j] = mn_rowpart * BN * 2 + ((cl ^ mn_s) * 16) + 8 * (i16 & 1);
             }
         }
     }
 
     // ---- global -> LDS: the loads of K tile t ---------------------------------
-    // Loads are numbered 0..LPT-1 (A's wave instructions, then B's).  Masking is
-    // branch-free: a chunk past M/N was given an out-of-range offset at setup; a
-    // chunk past K (the K tail, and every load of the padding tiles t >= KT) is
-    // masked per lane here.  Because q = j*4 + wave, a lane's swizzled K chunk is
-    // the same for all of its loads of one operand, so one compare per tile does.
-    template <int J0, int J1>
-    __device__ __forceinline__ void issue_range(int t, IGC_LDS char* stage) {
+    // Wave instructions J0 .. J1-1 of operand OP (0: A, 1: B) of tile t into its
+    // slot.  Masking is branch-free: a chunk past M/N was given an out-of-range
+    // offset at setup; a chunk past K (the K tail, and every load of the
+    // padding tiles t >= KT) is masked per lane here.  Because q = j*NW + wave,
+    // a lane's swizzled K chunk is the same for all of its loads of one
+    // operand, so one compare per tile does.
+    template <int OP, int J0, int J1>
+    __device__ __forceinline__ void issue_op(int t, IGC_LDS char* dst) {
         const int64_t k0 = kbase + (int64_t)t * BK;
-        IGC_LDS char* sa = stage;
-        IGC_LDS char* sb = stage + TA::BYTES;
-        const int64_t krem = kend - k0;  // valid K elements left from this tile on (may be <= 0)
+        IGC_LDS char* sa = dst;
+        IGC_LDS char* sb = dst;
+        // valid K elements left from this tile on, clamped to [0, BK] on the
+        // scalar side so the per-lane masks below are 32-bit compares
+        const int64_t krem64 = kend - k0;
+        const int krem = krem64 <= 0 ? 0 : (krem64 >= BK ? BK : (int)krem64);
         // ---- A
-        if constexpr (J0 < TA::IPW) {
+        if constexpr (OP == 0 && J1 > J0) {
             if constexpr (C::CONV) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A);
                 const bool uniform_tap = (p.Cin % BK) == 0;
@@ -356,7 +411,7 @@ struct Mainloop {
                     s = tap - r * p.S;
                     cbase = (int)(k0 - (int64_t)tap * p.Cin);
                 }
-                static_for<J0, (J1 < TA::IPW ? J1 : TA::IPW)>([&](auto J) __attribute__((always_inline)) {
+                static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     const int q = j * C::NW + wave;
                     const int c = TA::logical_chunk(q, lane);
@@ -378,13 +433,13 @@ struct Mainloop {
             } else if constexpr (C::A_KC) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (m0 * p.lda + k0) * 2);
                 const bool kout = 8 * ca_lane >= krem;
-                static_for<J0, (J1 < TA::IPW ? J1 : TA::IPW)>([&](auto J) __attribute__((always_inline)) {
+                static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     dma16(rs, sa + (j * C::NW + wave) * 1024, kout ? kOob : da.voff[j]);
                 });
             } else {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (k0 * p.lda + m0) * 2);
-                static_for<J0, (J1 < TA::IPW ? J1 : TA::IPW)>([&](auto J) __attribute__((always_inline)) {
+                static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     const int q = j * C::NW + wave;
                     dma16(rs, sa + q * 1024, TA::row_of(q, lane) >= krem ? kOob : da.voff[j]);
@@ -392,9 +447,8 @@ struct Mainloop {
             }
         }
         // ---- B
-        if constexpr (J1 > TA::IPW) {
-            constexpr int B0 = J0 > TA::IPW ? J0 - TA::IPW : 0;
-            constexpr int B1 = J1 - TA::IPW;
+        if constexpr (OP == 1 && J1 > J0) {
+            constexpr int B0 = J0, B1 = J1;
             if constexpr (C::B_KC) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (n0 * p.ldb + k0) * 2);
                 const bool kout = 8 * cb_lane >= krem;
@@ -413,20 +467,30 @@ struct Mainloop {
         }
     }
 
+    template <int OP>
+    static constexpr int ipw() { return OP == 0 ? TA::IPW : TB::IPW; }
+
     // All loads of tile t.  Tiles t >= KT are padding tiles: every load is out
     // of range, the slot fills with zeros and the MFMAs on it add exact zeros.
-    __device__ __forceinline__ void issue(int t, IGC_LDS char* stage) { issue_range<0, C::LPT>(t, stage); }
+    __device__ __forceinline__ void issue(int t, IGC_LDS char* sa, IGC_LDS char* sb) {
+        issue_op<0, 0, TA::IPW>(t, sa);
+        issue_op<1, 0, TB::IPW>(t, sb);
+    }
 
-    // Part PART of NPARTS of the loads of tile t.
-    template <int PART, int NPARTS>
-    __device__ __forceinline__ void issue_part(int t, IGC_LDS char* stage) {
-        issue_range<PART * C::LPT / NPARTS, (PART + 1) * C::LPT / NPARTS>(t, stage);
+    // Part PART of NPARTS of the loads of two ring units: operand OP1 of tile
+    // t1 into d1, then operand OP2 of tile t2 into d2 (numbered in that order).
+    template <int PART, int NPARTS, int OP1, int OP2>
+    __device__ __forceinline__ void issue_units_part(int t1, IGC_LDS char* d1, int t2, IGC_LDS char* d2) {
+        constexpr int N1 = ipw<OP1>(), N = N1 + ipw<OP2>();
+        constexpr int J0 = PART * N / NPARTS, J1 = (PART + 1) * N / NPARTS;
+        issue_op<OP1, (J0 < N1 ? J0 : N1), (J1 < N1 ? J1 : N1)>(t1, d1);
+        issue_op<OP2, (J0 > N1 ? J0 - N1 : 0), (J1 > N1 ? J1 - N1 : 0)>(t2, d2);
     }
 
     // After this wave's loads of K tile t have landed and before the barrier:
     // when K % 8 != 0, the chunk straddling K holds elements k >= K read from
     // beyond the row's end; the lane that fetched it zeroes them.
-    __device__ __forceinline__ void fixup_ragged_k(int t, IGC_LDS char* stage) {
+    __device__ __forceinline__ void fixup_ragged_k(int t, IGC_LDS char* sa, IGC_LDS char* sb) {
         const int64_t k0 = kbase + (int64_t)t * BK;
         if (!p.k_ragged8 || k0 + BK <= p.K) return;
         // the only chunk that straddles K is the one starting at k0 + 8*cs
@@ -453,14 +517,14 @@ struct Mainloop {
 #pragma unroll
             for (int j = 0; j < TA::IPW; ++j) {
                 const int q = j * C::NW + wave;
-                fix(stage, q, TA::logical_chunk(q, lane));
+                fix(sa, q, TA::logical_chunk(q, lane));
             }
         }
         if constexpr (C::B_KC) {
 #pragma unroll
             for (int j = 0; j < TB::IPW; ++j) {
                 const int q = j * C::NW + wave;
-                fix(stage + TA::BYTES, q, TB::logical_chunk(q, lane));
+                fix(sb, q, TB::logical_chunk(q, lane));
             }
         }
     }
@@ -470,9 +534,9 @@ struct Mainloop {
     // order in which the MFMAs of the k-step consume them.
     __device__ __forceinline__ void read_a(const IGC_LDS char* sa, int kk, int i, i16x8_t& f) {
         if constexpr (C::A_KC) {
-            f = *(const IGC_LDS i16x8_t*)(sa + fa_off[kk] + i * 32 * BK * 2);
+            f = *(const IGC_LDS i16x8_t*)(sa + fa_off[kk] + i * MI * BK * 2);
         } else {
-            const IGC_LDS char* a0 = sa + fa_off[i] + (16 * kk) * BM * 2;
+            const IGC_LDS char* a0 = sa + fa_off[i] + (KS * kk) * BM * 2;
             i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)a0);
             i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(a0 + 4 * BM * 2));
             f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -480,17 +544,16 @@ struct Mainloop {
     }
     __device__ __forceinline__ void read_b(const IGC_LDS char* sb, int kk, int j, i16x8_t& f) {
         if constexpr (C::B_KC) {
-            f = *(const IGC_LDS i16x8_t*)(sb + fb_off[kk] + j * 32 * BK * 2);
+            f = *(const IGC_LDS i16x8_t*)(sb + fb_off[kk] + j * MI * BK * 2);
         } else {
-            const IGC_LDS char* b0 = sb + fb_off[j] + (16 * kk) * BN * 2;
+            const IGC_LDS char* b0 = sb + fb_off[j] + (KS * kk) * BN * 2;
             i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)b0);
             i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)(b0 + 4 * BN * 2));
             f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     }
-    __device__ __forceinline__ void read_frags(const IGC_LDS char* stage, int kk, i16x8_t (&fa)[FM], i16x8_t (&fb)[FN]) {
-        const IGC_LDS char* sa = stage;
-        const IGC_LDS char* sb = stage + TA::BYTES;
+    __device__ __forceinline__ void read_frags(const IGC_LDS char* sa, const IGC_LDS char* sb, int kk,
+                                               i16x8_t (&fa)[FM], i16x8_t (&fb)[FN]) {
         read_a(sa, kk, 0, fa[0]);
 #pragma unroll
         for (int j = 0; j < FN; ++j) read_b(sb, kk, j, fb[j]);
@@ -500,7 +563,7 @@ struct Mainloop {
     // LDS read instructions of one k-step
     static constexpr int DS_READS = FM * (C::A_KC ? 1 : 2) + FN * (C::B_KC ? 1 : 2);
 
-    __device__ __forceinline__ static void mma(f32x16_t (&acc)[FM][FN], const i16x8_t (&fa)[FM], const i16x8_t (&fb)[FN]) {
+    __device__ __forceinline__ static void mma(Acc (&acc)[FM][FN], const i16x8_t (&fa)[FM], const i16x8_t (&fb)[FN]) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -524,21 +587,24 @@ struct Mainloop {
     }
 
     // ---- epilogue: accumulators -> C ---------------------------------------
-    __device__ __forceinline__ void store(const f32x16_t (&acc)[FM][FN], void* dst, int64_t ldc, int kind,
+    // Lane l holds, of block (i, j), row MI*i + l%MI and, in accumulators
+    // 4g..4g+3, the 4 consecutive columns MI*j + 4*NH*g + 4*(l/MI) + 0..3.
+    __device__ __forceinline__ void store(const Acc (&acc)[FM][FN], void* dst, int64_t ldc, int kind,
                                           bool vec_ok) {
+        constexpr int NG = MI == 32 ? 4 : 1;  // groups of 4 accumulators per block
         const bool full = vec_ok && (m0 + BM <= p.M) && (n0 + BN <= p.N);
-        const int64_t mrow = m0 + wm * C::WTM + (lane & 31);
-        const int64_t ncol = n0 + wn * C::WTN + 4 * (lane >> 5);
+        const int64_t mrow = m0 + wm * C::WTM + (lane % MI);
+        const int64_t ncol = n0 + wn * C::WTN + 4 * (lane / MI);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int64_t m = mrow + 32 * i;
+            const int64_t m = mrow + MI * i;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                // one 32x32 block at a time: only 16 accumulators move to VGPRs at once
+                // one block at a time: only its accumulators move to VGPRs at once
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t n = ncol + 32 * j + 8 * g;
+                for (int g = 0; g < NG; ++g) {
+                    const int64_t n = ncol + MI * j + 4 * NH * g;
                     const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
                     const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
                     const int64_t off = m * ldc + n;
@@ -624,18 +690,23 @@ __device__ __forceinline__ void interleave() {
     });
 }
 
-// LDS slot U of the stage ring of configuration C: one __shared__ array per
-// slot, so every slot is a distinct object to the compiler.
-template <class C, int U>
-__device__ __forceinline__ IGC_LDS char* stage() {
-    __shared__ __attribute__((aligned(1024))) char buf[C::STAGE_BYTES];
+// LDS slot S of the ring of configuration C: one __shared__ array per slot,
+// so every slot is a distinct object to the compiler.
+template <class C, int S>
+__device__ __forceinline__ IGC_LDS char* slot() {
+    __shared__ __attribute__((aligned(1024))) char buf[C::template slot_bytes<S>()];
     return (IGC_LDS char*)buf;
 }
+// Slots of operand A and B of the u-th tile of an unrolled period.
+template <class C, int u>
+__device__ __forceinline__ IGC_LDS char* slot_a() { return slot<C, Ring::slot_of(C::U, 2 * u)>(); }
+template <class C, int u>
+__device__ __forceinline__ IGC_LDS char* slot_b() { return slot<C, Ring::slot_of(C::U, 2 * u + 1)>(); }
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     using ML = Mainloop<C>;
-    constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN;
+    constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN, U = C::U, P = C::P;
 
     // workgroups s*T .. s*T+T-1 (T output tiles) take K split s
     const int T = p.tiles_m * p.tiles_n;
@@ -647,107 +718,145 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN, kbase, kend);
     const int KT = ml.KT, KTp = ml.KTp;
 
-    f32x16_t acc[FM][FN];
+    typename C::Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < FN; ++j) acc[i][j] = typename C::Acc{};
+    // Two fragment register sets: k-step kk of the u-th tile of a period uses
+    // set (u*KK + kk) % 2, while the next k-step's fragments load into the other.
     i16x8_t fa[2][FM], fb[2][FN];
 
     // The accumulators are never updated under a branch: every K tile of the
     // padded loop runs the same MFMA sequence, so no copies of them are needed.
     constexpr int NMF = FM * FN;
     constexpr int DSR = ML::DS_READS;
-    if constexpr (D >= 2 && C::SPREAD) {
-        // ---- prologue: tiles 0 .. D-2; slot D-1 is refilled during tile 0
-        static_for<0, D - 1>([&](auto S) __attribute__((always_inline)) { ml.issue(S, stage<C, S>()); });
-        ml.template wait_tiles<D - 2>(D - 2);
-        ml.fixup_ragged_k(0, stage<C, 0>());
+    // The loop is compiled twice: with the K % 8 fixup between each tile's wait
+    // and barrier (RAGGED), and without it, so the common case carries no
+    // branch inside the loop.
+    auto kloop = [&](auto ragged) __attribute__((always_inline)) {
+    constexpr bool RAGGED = decltype(ragged)::value;
+    auto fixup = [&](int t, IGC_LDS char* sa, IGC_LDS char* sb) __attribute__((always_inline)) {
+        if constexpr (RAGGED) ml.fixup_ragged_k(t, sa, sb);
+    };
+    if constexpr (C::SPREAD) {
+        // ---- operand-slot ring (ring.hpp): unit s = operand s%2 of tile s/2 in
+        // slot s % U.  Prologue: units 0 .. U-3; during tile t the units
+        // 2t+U-2 and 2t+U-1 (the slots of tile t-1, freed by the barrier that
+        // made tile t ready) are refilled by loads spread over its k-steps.
+        constexpr int WAITN = Ring::wait_loads(U, ML::template ipw<0>(), ML::template ipw<1>());
+        static_for<0, U - 2>([&](auto S) __attribute__((always_inline)) {
+            constexpr int s = S;
+            ml.template issue_op<s % 2, 0, ML::template ipw<s % 2>()>(s / 2, slot<C, s>());
+        });
+        wait_vmcnt<WAITN>();
+        fixup(0, slot_a<C, 0>(), slot_b<C, 0>());
         ring_barrier();
-        ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
-        for (int t0 = 0; t0 < KTp; t0 += D) {
-            static_for<0, D>([&](auto U) __attribute__((always_inline)) {
-                constexpr int u = U;
-                constexpr int un = (u + 1) % D;
-                constexpr int uf = (u + D - 1) % D;  // slot of tile t-1, freed by the last barrier
+        ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
+        for (int t0 = 0; t0 < KTp; t0 += P) {
+            static_for<0, P>([&](auto UU) __attribute__((always_inline)) {
+                constexpr int u = UU;
                 const int t = t0 + u;
-                // k-steps 0 .. KK-2: refill slot uf with tile t+D-1, read ahead, MFMA
-                static_for<0, KK - 1>([&](auto KS) __attribute__((always_inline)) {
-                    constexpr int kk = KS;
-                    ml.template issue_part<kk, KK>(t + D - 1, stage<C, uf>());
-                    ml.read_frags(stage<C, u>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-                    ML::mma(acc, fa[kk & 1], fb[kk & 1]);
+                // the two units refilled during tile t
+                constexpr int s1 = 2 * u + U - 2, s2 = 2 * u + U - 1;
+                constexpr int op1 = s1 % 2, op2 = s2 % 2;
+                const int t1 = t + (U - 2 - op1) / 2, t2 = t + (U - 1 - op2) / 2;
+                IGC_LDS char* d1 = slot<C, Ring::slot_of(U, s1)>();
+                IGC_LDS char* d2 = slot<C, Ring::slot_of(U, s2)>();
+                constexpr int p0 = (u * KK) & 1;  // fragment set of this tile's k-step 0
+                // k-steps 0 .. KK-2: refill, read ahead, MFMA
+                static_for<0, KK - 1>([&](auto KI) __attribute__((always_inline)) {
+                    constexpr int kk = KI;
+                    constexpr int pc = (p0 + kk) & 1, pn = pc ^ 1;
+                    ml.template issue_units_part<kk, KK, op1, op2>(t1, d1, t2, d2);
+                    ml.read_frags(slot_a<C, u>(), slot_b<C, u>(), kk + 1, fa[pn], fb[pn]);
+                    ML::mma(acc, fa[pc], fb[pc]);
                     interleave<NMF, DSR, C::LPT / KK>();
                     __builtin_amdgcn_sched_barrier(0);
                 });
-                ml.template issue_part<KK - 1, KK>(t + D - 1, stage<C, uf>());
-                // ready(t+1) and free(t): D-2 newer tiles may stay in flight
-                ml.template wait_tiles<D - 2>(D - 2);
-                ml.fixup_ragged_k(t + 1, stage<C, un>());
+                constexpr int pl = (p0 + KK - 1) & 1;  // set of the last k-step; the next tile's first uses pl^1
+                ml.template issue_units_part<KK - 1, KK, op1, op2>(t1, d1, t2, d2);
+                // ready(t+1) and free(t): the units newer than B(t+1) may stay in flight
+                wait_vmcnt<WAITN>();
+                fixup(t + 1, slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>());
                 ring_barrier();
-                ml.read_frags(stage<C, un>(), 0, fa[0], fb[0]);
-                ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+                ml.read_frags(slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
+                ML::mma(acc, fa[pl], fb[pl]);
                 interleave<NMF, DSR, 0>();
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
         wait_vmcnt<0>();  // the padding tiles past the loop are still landing in free slots
     } else if constexpr (D >= 2) {
-        // ---- prologue: fill the ring
+        // ---- two stages, refilled in one burst right after the barrier
         static_for<0, D>([&](auto S) __attribute__((always_inline)) {
-            if (S < KTp) ml.issue(S, stage<C, S>());
+            if (S < KTp) ml.issue(S, slot_a<C, S>(), slot_b<C, S>());
         });
         ml.template wait_tiles<D - 1>(Ring::inflight_after(D, KTp, 0));
-        ml.fixup_ragged_k(0, stage<C, 0>());
+        fixup(0, slot_a<C, 0>(), slot_b<C, 0>());
         ring_barrier();
-        ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+        ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
         // ---- steady state, unrolled by D so every slot is a constant
         for (int t0 = 0; t0 < KTp; t0 += D) {
-            static_for<0, D>([&](auto U) __attribute__((always_inline)) {
-                constexpr int u = U;
+            static_for<0, D>([&](auto UU) __attribute__((always_inline)) {
+                constexpr int u = UU;
                 constexpr int un = (u + 1) % D;
                 const int t = t0 + u;
-                static_for<0, KK - 1>([&](auto KS) __attribute__((always_inline)) {
-                    constexpr int kk = KS;
-                    ml.read_frags(stage<C, u>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-                    ML::mma(acc, fa[kk & 1], fb[kk & 1]);
+                constexpr int p0 = (u * KK) & 1;  // fragment set of this tile's k-step 0
+                static_for<0, KK - 1>([&](auto KI) __attribute__((always_inline)) {
+                    constexpr int kk = KI;
+                    constexpr int pc = (p0 + kk) & 1, pn = pc ^ 1;
+                    ml.read_frags(slot_a<C, u>(), slot_b<C, u>(), kk + 1, fa[pn], fb[pn]);
+                    ML::mma(acc, fa[pc], fb[pc]);
                     interleave<NMF, DSR, 0>();
                     __builtin_amdgcn_sched_barrier(0);  // k-steps stay in order: two fragment sets live
                 });
+                constexpr int pl = (p0 + KK - 1) & 1;
                 // ready(t+1): own loads landed, then everyone; free(t): all reads of t done.
                 // After the last tile this is a harmless extra barrier and read.
                 ml.template wait_tiles<D - 2>(Ring::inflight_after(D, KTp, t + 1));
-                ml.fixup_ragged_k(t + 1, stage<C, un>());
+                fixup(t + 1, slot_a<C, un>(), slot_b<C, un>());
                 ring_barrier();
-                if (t + D < KTp) ml.issue(t + D, stage<C, u>());
-                ml.read_frags(stage<C, un>(), 0, fa[0], fb[0]);
-                ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+                if (t + D < KTp) ml.issue(t + D, slot_a<C, u>(), slot_b<C, u>());
+                ml.read_frags(slot_a<C, un>(), slot_b<C, un>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
+                ML::mma(acc, fa[pl], fb[pl]);
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
     } else {
         // ---- D == 1: one slot, no overlap of loads with compute
-        if (KT > 0) ml.issue(0, stage<C, 0>());
+        static_assert(D != 1 || KK % 2 == 0, "the unpipelined loop alternates fragment sets within a tile");
+        IGC_LDS char* sa = slot_a<C, 0>();
+        IGC_LDS char* sb = slot_b<C, 0>();
+        if (KT > 0) ml.issue(0, sa, sb);
         wait_vmcnt<0>();
-        ml.fixup_ragged_k(0, stage<C, 0>());
+        fixup(0, sa, sb);
         ring_barrier();
-        ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+        ml.read_frags(sa, sb, 0, fa[0], fb[0]);
         for (int t = 0; t < KT; ++t) {
-            static_for<0, KK - 1>([&](auto KS) __attribute__((always_inline)) {
-                constexpr int kk = KS;
-                ml.read_frags(stage<C, 0>(), kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            static_for<0, KK - 1>([&](auto KI) __attribute__((always_inline)) {
+                constexpr int kk = KI;
+                ml.read_frags(sa, sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 ML::mma(acc, fa[kk & 1], fb[kk & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             });
             ring_barrier();  // free: every wave has read tile t
-            if (t + 1 < KT) ml.issue(t + 1, stage<C, 0>());
+            if (t + 1 < KT) ml.issue(t + 1, sa, sb);
             wait_vmcnt<0>();
-            ml.fixup_ragged_k(t + 1, stage<C, 0>());
+            fixup(t + 1, sa, sb);
             ring_barrier();  // ready: tile t+1 landed for every wave
-            ml.read_frags(stage<C, 0>(), 0, fa[0], fb[0]);
+            ml.read_frags(sa, sb, 0, fa[0], fb[0]);
             ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    };
+    if constexpr (C::CONV) {
+        kloop(std::false_type{});  // channels are a multiple of 8: never ragged
+    } else if (p.k_ragged8) {
+        kloop(std::true_type{});
+    } else {
+        kloop(std::false_type{});
     }
     // ---- output epilogue: nothing is in flight any more
     if (p.k_splits > 1)

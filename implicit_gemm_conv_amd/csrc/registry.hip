@@ -4,14 +4,14 @@
 namespace igc {
 
 static const igc_tune_t kTunes[] = {
-#define IGC_TUNE_ENTRY(BM, BN, BK, D, W) {BM, BN, BK, D, W, 0},
+#define IGC_TUNE_ENTRY(BM, BN, BK, D, W, MI, H) {BM, BN, BK, D, W, MI, H, 0},
     IGC_FOR_EACH_TILE(IGC_TUNE_ENTRY)
 #undef IGC_TUNE_ENTRY
 };
 
 typedef const Instance* (*TableFn)(int*);
 static const TableFn kTables[] = {
-#define IGC_TABLE_ENTRY(BM, BN, BK, D, W) &instance_table_##BM##x##BN##x##BK##x##D##x##W,
+#define IGC_TABLE_ENTRY(BM, BN, BK, D, W, MI, H) &instance_table_##BM##x##BN##x##BK##x##D##x##W##x##MI##x##H,
     IGC_FOR_EACH_TILE(IGC_TABLE_ENTRY)
 #undef IGC_TABLE_ENTRY
 };
@@ -21,13 +21,14 @@ int num_tunes() { return (int)(sizeof(kTunes) / sizeof(kTunes[0])); }
 igc_tune_t tune_at(int i) { return kTunes[i]; }
 
 const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_kc, bool conv) {
+    const int mfma = q.mfma == 0 ? 32 : q.mfma;
     for (TableFn fn : kTables) {
         int n = 0;
         const Instance* t = fn(&n);
         for (int i = 0; i < n; ++i) {
             const Instance& e = t[i];
             if (e.bm == q.bm && e.bn == q.bn && e.bk == q.bk && e.d == q.pipe_depth && e.waves == q.waves &&
-                e.fp16 == fp16 && e.a_kc == a_kc && e.b_kc == b_kc && e.conv == conv)
+                e.mfma == mfma && e.half == q.half_stage && e.fp16 == fp16 && e.a_kc == a_kc && e.b_kc == b_kc && e.conv == conv)
                 return &e;
         }
     }
@@ -38,9 +39,10 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
     (void)conv;
     constexpr int64_t kCUs = 256;
     // Enough 256x256 tiles for every CU: the largest tile (least global and LDS
-    // traffic per flop), 8 waves, a 4-stage ring of 32-deep K tiles.
+    // traffic per flop), 8 waves, a 4-stage ring of 32-deep K tiles, 16x16x32
+    // MFMAs (which sustain a higher clock than 32x32x16 under full load).
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= kCUs) return igc_tune_t{256, 256, 32, 4, 8, 1};
+    if (t256 >= kCUs) return igc_tune_t{256, 256, 32, 4, 8, 16, 0, 1};
     // Otherwise 128x128 tiles, and split K until every CU has a workgroup
     // (each split keeps at least 2048 of K).
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
@@ -51,7 +53,7 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
         if (S > 16) S = 16;
         if (S < 1) S = 1;
     }
-    return igc_tune_t{128, 128, 64, 4, 4, (int)S};
+    return igc_tune_t{128, 128, 64, 4, 4, 32, 0, (int)S};
 }
 
 }  // namespace igc

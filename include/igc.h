@@ -58,14 +58,17 @@ typedef enum { IGC_OUT_F32 = 0, IGC_OUT_BF16 = 1, IGC_OUT_F16 = 2 } igc_out_t;
 
 /* Optional tuning: output tile BM x BN, K tile BK, PIPE_DEPTH = number of LDS
  * stages in the ring, the number of wave64s per workgroup (4: one per SIMD;
- * 8: two per SIMD), and k_splits (<= 1: none; S > 1: split K into up to S
+ * 8: two per SIMD), the MFMA block edge (32: v_mfma_f32_32x32x16, 16:
+ * v_mfma_f32_16x16x32; 0 means 32), half_stage (1: the ring holds one more
+ * operand tile, A or B, than PIPE_DEPTH whole stages, i.e. 2*PIPE_DEPTH+1
+ * operand slots), and k_splits (<= 1: none; S > 1: split K into up to S
  * ranges computed by separate workgroups whose fp32 partial tiles are summed
  * in split order by a second kernel).  Only compiled (bm, bn, bk, pipe_depth,
- * waves) combinations are accepted (see igc_tune_supported); NULL selects the
- * built-in choice for the shape (which splits K when the output has too few
- * tiles to occupy every CU). */
+ * waves, mfma, half_stage) combinations are accepted (see
+ * igc_tune_supported); NULL selects the built-in choice for the shape (which
+ * splits K when the output has too few tiles to occupy every CU). */
 typedef struct {
-    int bm, bn, bk, pipe_depth, waves, k_splits;
+    int bm, bn, bk, pipe_depth, waves, mfma, half_stage, k_splits;
 } igc_tune_t;
 
 /*
@@ -126,7 +129,7 @@ igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int
                                           const void *x, const void *w, void *y, igc_out_t y_type, int fp16,
                                           const igc_tune_t *tune, igc_stream_t stream);
 
-/* 1 if (bm, bn, bk, pipe_depth, waves) is a compiled configuration, else 0. */
+/* 1 if (bm, bn, bk, pipe_depth, waves, mfma, half_stage) is a compiled configuration, else 0. */
 int igc_tune_supported(const igc_tune_t *tune);
 
 /* The configuration the library picks for an M x N x K problem (conv != 0: the
@@ -145,28 +148,35 @@ const char *igc_status_string(igc_status_t status);
 
 /*
  * Ring schedule of the mainloop, for inspection and testing on the host.
- * For a K loop of `k_tiles` tiles and a ring of `pipe_depth` stages, writes up
- * to `cap` events into `events` as int triples (kind, tile, slot):
- *   kind 0 = issue the loads of `tile` into `slot`,
- *   kind 1 = wait until `tile` has landed (each wave waits on its own loads,
- *            then the workgroup barrier runs; `slot` is the value passed to the
- *            wave's s_waitcnt vmcnt, i.e. how many of its loads may still be
- *            in flight, counted in tiles),
- *   kind 2 = read `tile` from `slot` (fragment loads + MFMA).
- *   kind 3 = workgroup barrier only (D == 1 frees its single slot with it;
- *            every schedule ends with one once nothing is left in flight).
- * For pipe_depth >= 2 the K loop is padded to a multiple of pipe_depth with
- * tiles whose loads are all out of range (they land as zeros and add nothing),
- * so tiles up to that padded count appear.  For pipe_depth >= 3 the prologue
- * issues pipe_depth-1 tiles and, during each tile t, the loads of tile
- * t+pipe_depth-1 are issued (interleaved with t's MFMAs) into the slot the last
- * barrier freed; tiles past the padded count are issued out of range and never
- * read.  Each wave drains its own LDS reads
- * before every barrier, so a barrier after a tile's reads frees its slot.
- * Returns the number of events (which may exceed cap), or -1 on bad input.
- * This is the exact sequence the kernels execute.
+ * The LDS ring holds U = 2*pipe_depth + half_stage operand slots; the K loop
+ * consumes units, unit 2t being the A tile and unit 2t+1 the B tile of K tile
+ * t, and unit s always lives in slot s % U.  For a K loop of `k_tiles` tiles,
+ * writes up to `cap` events into `events` as int quadruples
+ * (kind, tile, operand, x):
+ *   kind 0 = issue the loads of operand `operand` (0: A, 1: B) of `tile` into
+ *            slot x,
+ *   kind 1 = wait until both operands of `tile` have landed (each wave waits
+ *            on its own loads, then the workgroup barrier runs); x is how many
+ *            newer units the wave's s_waitcnt vmcnt lets stay in flight
+ *            (operand is -1),
+ *   kind 2 = read operand `operand` of `tile` from slot x (fragment loads,
+ *            then MFMAs),
+ *   kind 3 = workgroup barrier only (pipe_depth 1 frees its single stage with
+ *            it; every schedule ends with one once nothing is left in flight).
+ * The K loop is padded to a whole number of ring periods (U tiles for an odd
+ * U, U/2 for an even one; no padding for pipe_depth 1) with tiles whose loads
+ * are all out of range: they land as zeros and add nothing, so tiles up to
+ * that padded count appear.  Rings of five or more slots issue units 0..U-3
+ * up front and, during each tile t, units 2t+U-2 and 2t+U-1 (interleaved with
+ * t's MFMAs) into the two slots the last barrier freed; units past the padded
+ * count are issued out of range and never read.  Two-stage rings issue tile
+ * t+2 right after the barrier that frees tile t.  Each wave drains its own
+ * LDS reads before every barrier, so a barrier after a unit's reads frees its
+ * slot.  Returns the number of events (which may exceed cap), or -1 on bad
+ * input (pipe_depth outside 1..8, half_stage not 0/1 or with pipe_depth 1,
+ * negative k_tiles or cap).  This is the exact sequence the kernels execute.
  */
-int igc_ring_schedule(int pipe_depth, int k_tiles, int *events, int cap);
+int igc_ring_schedule(int pipe_depth, int half_stage, int k_tiles, int *events, int cap);
 
 /*
  * LDS swizzle of the operand tiles, for inspection and testing on the host.

@@ -98,23 +98,29 @@ def test_conv_validation(args, expect):
 def test_tune_table_fits_lds():
     """Every compiled ring fits the 160 KB of LDS of one CU (a stage costs (BM+BN)*BK*2 bytes)."""
     tunes = igc.tunes()
-    assert (256, 256, 64, 2, 4) in tunes and (256, 256, 32, 5, 8) in tunes
-    for (bm, bn, bk, d, w) in tunes:
-        lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w))
-        assert lds == (bm + bn) * bk * 2 * d
+    assert (256, 256, 64, 2, 4, 32, 0) in tunes and (256, 256, 32, 5, 8, 32, 0) in tunes
+    assert (256, 256, 32, 4, 8, 16, 0) in tunes and (256, 256, 64, 2, 4, 16, 1) in tunes
+    for (bm, bn, bk, d, w, mi, h) in tunes:
+        lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h))
+        U = 2 * d + h
+        assert lds == ((bm + bn) * bk * 2 * d if U % 2 == 0 else U * max(bm, bn) * bk * 2)
         assert lds <= 160 * 1024
-        assert igc.igc_tune_supported((bm, bn, bk, d, w)) == 1
+        assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h)) == 1
     assert igc.igc_tune_supported((256, 256, 64, 3, 4)) == 0  # 192 KB: over budget, not compiled
     assert igc.igc_tune_supported((256, 256, 64, 2, 6)) == 0
+    assert igc.igc_tune_supported((256, 256, 32, 4, 8, 8)) == 0  # no 8x8 MFMA block
+    # mfma 0 selects the 32x32x16 instance
+    assert igc.igc_tune_supported((256, 256, 32, 5, 8, 0)) == 1
+    assert igc.igc_tune_supported((256, 256, 32, 5, 8, 16)) == 0  # 5 stages x 1 k-step: odd fragment parity
 
 
 @pytest.mark.parametrize("shape,expect", [
-    ((8192, 8192, 8192), ((256, 256, 32, 4, 8), 1)),      # enough 256x256 tiles for 256 CUs: no split
-    ((100352, 256, 2304), ((256, 256, 32, 4, 8), 1)),     # the 3x3 conv's GEMM view
-    ((2048, 1024, 16384), ((128, 128, 64, 4, 4), 2)),     # 128 tiles of 128x128: split K in two
-    ((1000, 1000, 65536), ((128, 128, 64, 4, 4), 4)),     # 64 tiles: four splits
-    ((128, 96, 200), ((128, 128, 64, 4, 4), 1)),          # too little K to split
-    ((0, 5, 7), ((128, 128, 64, 4, 4), 1)),
+    ((8192, 8192, 8192), ((256, 256, 32, 4, 8, 16, 0), 1)),      # enough 256x256 tiles for 256 CUs: no split
+    ((100352, 256, 2304), ((256, 256, 32, 4, 8, 16, 0), 1)),     # the 3x3 conv's GEMM view
+    ((2048, 1024, 16384), ((128, 128, 64, 4, 4, 32, 0), 2)),     # 128 tiles of 128x128: split K in two
+    ((1000, 1000, 65536), ((128, 128, 64, 4, 4, 32, 0), 4)),     # 64 tiles: four splits
+    ((128, 96, 200), ((128, 128, 64, 4, 4, 32, 0), 1)),          # too little K to split
+    ((0, 5, 7), ((128, 128, 64, 4, 4, 32, 0), 1)),
 ])
 def test_default_tune(shape, expect):
     t = igc.igc_default_tune(*shape)
@@ -125,76 +131,121 @@ def test_default_tune(shape, expect):
 ISSUE, WAIT, READ, BARRIER = 0, 1, 2, 3
 
 
-def simulate_ring(D, KT):
-    """Checks the ready/free protocol of the schedule the kernels run.
+def simulate_ring(D, KT, half=0):
+    """Checks the ready/free protocol of the schedule the kernels run, in units
+    (unit 2t = A tile of K tile t, unit 2t+1 = its B tile) over U = 2D + half
+    operand slots:
 
-    * every tile of the (padded) K loop is issued exactly once, into slot
-      tile % D, and read exactly once, in order;
+    * every unit of the (padded) K loop is issued exactly once, into slot
+      unit % U, and read exactly once; tiles are read in order;
     * a tile is read only after a wait for it, and that wait allows exactly the
-      number of newer tiles this wave issued after it (loads complete in order),
-      so the tile has landed for every wave once the barrier passes;
+      number of newer units this wave issued after the tile's B unit (loads
+      complete in order), so both operands have landed for every wave once
+      the barrier passes;
     * a slot is reloaded only after a barrier that follows the last read of the
-      tile it held (each wave drains its reads before the barrier);
-    * never more than D tiles occupy the ring.
+      unit it held (each wave drains its reads before the barrier);
+    * never more than U units occupy the ring.
     """
-    ev = igc.igc_ring_schedule(D, KT)
-    issued, read, waited = [], [], set()
-    slot_tile = {}
-    slot_freed = {}  # slot -> True once a barrier followed the last read of its tile
-    last_read_slot = None
-    for kind, tile, x in ev:
+    U = 2 * D + half
+    ev = igc.igc_ring_schedule(D, KT, half)
+    issued, read_units, waited = [], set(), set()
+    slot_unit = {}
+    slot_freed = {}  # slot -> True once a barrier followed the last read of its unit
+    pending_free = []
+    tiles_read = []
+    for kind, tile, op, x in ev:
         if kind == ISSUE:
-            assert tile not in issued, f"tile {tile} issued twice"
-            assert x == tile % D
-            if x in slot_tile:
-                assert slot_tile[x] in read and slot_freed.get(x), f"slot {x} reloaded before tile {slot_tile[x]} was freed"
-            slot_tile[x] = tile
+            u = 2 * tile + op
+            assert u not in issued, f"unit {u} issued twice"
+            assert x == u % U, f"unit {u} into slot {x}"
+            if x in slot_unit:
+                assert slot_unit[x] in read_units or slot_unit[x] // 2 >= KTp_of(D, half, KT), \
+                    f"slot {x} reloaded before unit {slot_unit[x]} was read"
+                assert slot_freed.get(x), f"slot {x} reloaded before unit {slot_unit[x]} was freed"
+            slot_unit[x] = u
             slot_freed[x] = False
-            live = [t for t in issued if t not in read and t < tile] + [tile]
-            assert len(live) <= D
-            issued.append(tile)
+            live = [v for v in issued if v not in read_units and v < u] + [u]
+            assert len(live) <= U
+            issued.append(u)
         elif kind in (WAIT, BARRIER):
-            # the barrier frees the slot whose reads are finished
-            if last_read_slot is not None:
-                slot_freed[last_read_slot] = True
-                last_read_slot = None
+            # the barrier frees the slots whose reads are finished
+            for sl in pending_free:
+                slot_freed[sl] = True
+            pending_free = []
             if kind == WAIT:
-                newer = [t for t in issued if t > tile]
-                assert tile in issued, f"wait for tile {tile} never issued"
-                assert x == len(newer), f"wait({tile}) allows {x} newer tiles, {len(newer)} issued"
+                assert 2 * tile + 1 in issued and 2 * tile in issued, f"wait for tile {tile} never issued"
+                newer = [v for v in issued if v > 2 * tile + 1]
+                assert x == len(newer), f"wait({tile}) allows {x} newer units, {len(newer)} issued"
                 waited.add(tile)
         elif kind == READ:
+            u = 2 * tile + op
             assert tile in waited, f"tile {tile} read before its wait"
-            assert slot_tile.get(x) == tile, f"slot {x} does not hold tile {tile}"
-            assert tile == len(read), "tiles read out of order"
-            read.append(tile)
-            last_read_slot = x
-    KTp = KT if D == 1 else -(-KT // D) * D  # padded with zero-filled tiles
-    assert read == list(range(KTp))
-    # rings of 3+ stages also issue (out-of-range, never read) tiles past the padded loop
-    extra = [t for t in issued if t >= KTp]
-    assert sorted(t for t in issued if t < KTp) == list(range(KTp))
-    assert all(t < KTp + D - 1 for t in extra) and (D >= 3 or not extra)
+            assert slot_unit.get(x) == u, f"slot {x} does not hold unit {u}"
+            if op == 0:
+                assert tile == len(tiles_read), "tiles read out of order"
+                tiles_read.append(tile)
+            read_units.add(u)
+            pending_free.append(x)
+    KTp = KTp_of(D, half, KT)
+    assert tiles_read == list(range(KTp))
+    assert sorted(v for v in issued if v < 2 * KTp) == list(range(2 * KTp))
+    # spread rings also issue (out-of-range, never read) units past the padded loop
+    extra = [v for v in issued if v >= 2 * KTp]
+    assert all(v < 2 * KTp + U - 2 for v in extra) and (U >= 5 or not extra)
 
 
-@pytest.mark.parametrize("D", range(1, 9))
-def test_ring_protocol(D):
-    for KT in range(0, 3 * D + 3):
-        simulate_ring(D, KT)
+def KTp_of(D, half, KT):
+    U = 2 * D + half
+    period = 1 if D == 1 else (U if U % 2 else U // 2)
+    return -(-KT // period) * period
+
+
+RINGS = [(D, 0) for D in range(1, 9)] + [(D, 1) for D in range(2, 8)]
+
+
+@pytest.mark.parametrize("D,half", RINGS)
+def test_ring_protocol(D, half):
+    for KT in range(0, 3 * (2 * D + half) + 3):
+        simulate_ring(D, KT, half)
 
 
 def test_ring_protocol_catches_a_short_wait(monkeypatch):
-    """A schedule whose wait allows one tile too many in flight must fail the checker."""
+    """A schedule whose wait allows one unit too many in flight must fail the checker."""
     real = igc.igc_ring_schedule
 
-    def broken(D, KT):
-        return [(k, t, x + 1) if k == WAIT else (k, t, x) for (k, t, x) in real(D, KT)]
+    def broken(D, KT, half=0):
+        return [(k, t, o, x + 1) if k == WAIT else (k, t, o, x) for (k, t, o, x) in real(D, KT, half)]
+
+    monkeypatch.setattr(igc, "igc_ring_schedule", broken)
+    for D, half in ((3, 0), (2, 1)):
+        with pytest.raises(AssertionError):
+            simulate_ring(D, 8, half)
+
+
+def test_ring_protocol_catches_an_early_refill(monkeypatch):
+    """Moving a refill ahead of the barrier that frees its slot must fail the checker."""
+    real = igc.igc_ring_schedule
+
+    def broken(D, KT, half=0):
+        ev = real(D, KT, half)
+        for i in range(1, len(ev)):
+            if ev[i][0] == ISSUE and ev[i - 1][0] == READ and ev[i][1] > 1:
+                # swap the refill with the read before it, then with the wait before that
+                j = i
+                while j > 0 and ev[j - 1][0] != WAIT:
+                    ev[j - 1], ev[j] = ev[j], ev[j - 1]
+                    j -= 1
+                ev[j - 1], ev[j] = ev[j], ev[j - 1]
+                return ev
+        raise AssertionError("no refill found")
 
     monkeypatch.setattr(igc, "igc_ring_schedule", broken)
     with pytest.raises(AssertionError):
-        simulate_ring(3, 8)
+        simulate_ring(2, 8, 1)
 
 
 def test_ring_rejects_bad_args():
     with pytest.raises(ValueError):
         igc.igc_ring_schedule(0, 4)
+    with pytest.raises(ValueError):
+        igc.igc_ring_schedule(1, 4, 1)

@@ -164,9 +164,13 @@ def compiled_tunes():
 
 @pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
 def test_k_tiles_sweep(tune):
-    """K_TILES in {1, D-1, D, D+1, 2D, 2D+1} plus a ragged tail, for each pipeline depth D."""
-    bm, bn, bk, d, _ = tune
-    kts = sorted({1, max(d - 1, 1), d, d + 1, 2 * d, 2 * d + 1})
+    """K_TILES around one and two ring periods P (P = D stages, or 2D+1 tiles for a ring with an extra operand
+    slot) and around the slot count U, each whole and with a ragged tail."""
+    bm, bn, bk, d = tune[:4]
+    half = tune[6] if len(tune) > 6 else 0
+    U = 2 * d + half
+    P = 1 if d == 1 else (U if U % 2 else U // 2)
+    kts = sorted({1, max(P - 1, 1), P, P + 1, 2 * P, 2 * P + 1, max(U - 2, 1), U - 1, U})
     for j, kt in enumerate(kts):
         for K in (kt * bk, kt * bk - 24):
             if K <= 0:
@@ -178,13 +182,15 @@ def test_k_tiles_sweep(tune):
 
 @pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
 def test_k_chain_tags(tune):
-    """A = 1, b_kj = (floor(k/64) mod 5) + 1: C = sum_k tag(k) exactly.  Reading a stale ring slot (tile
-    t - D instead of t) changes the sum; dropping or repeating a K tile does too."""
-    bm, bn, bk, d, _ = tune
-    for K in (bk * (2 * d + 3), 1000):
+    """A = 1, b_kj = (floor(k/32) mod 7) + 1: C = sum_k tag(k) exactly.  Reading a stale ring slot (an older
+    tile's A or B instead of tile t's) changes the sum for every ring compiled here (fewer than 7 tiles back);
+    dropping or repeating a K tile does too."""
+    bm, bn, bk, d = tune[:4]
+    half = tune[6] if len(tune) > 6 else 0
+    for K in (bk * (2 * (2 * d + half) + 3), 1000):
         M, N = 130, 136  # row-major B: N * 2 bytes must be a multiple of 16
         A = np.full((M, K), 0x3F80, np.uint16)
-        tags = np.array([(k // 64) % 5 + 1 for k in range(K)], np.float32)
+        tags = np.array([(k // 32) % 7 + 1 for k in range(K)], np.float32)
         B = torch.from_numpy(np.repeat(tags[:, None], N, axis=1)).to(torch.bfloat16).view(torch.int16).numpy()
         B = B.view(np.uint16)
         say(f"k-chain tune {tune} K={K}")
@@ -192,7 +198,9 @@ def test_k_chain_tags(tune):
         assert np.all(y == float(tags.sum())), f"k-chain tune={tune} K={K}: {np.unique(y)[:5]}"
 
 
-@pytest.mark.parametrize("tune", [(128, 128, 64, 4, 4), (256, 256, 32, 4, 8), (256, 128, 64, 3, 4)])
+@pytest.mark.parametrize("tune", [(128, 128, 64, 4, 4, 32, 0), (256, 256, 32, 4, 8, 32, 0), (256, 128, 64, 3, 4, 32, 0),
+                                  (256, 256, 32, 4, 8, 16, 0), (128, 128, 64, 4, 4, 16, 0),
+                                  (256, 256, 64, 2, 4, 16, 1)])
 def test_split_k(tune):
     """K split over 2..8 workgroups per tile, fp32 partials summed in split order: ragged K, every layout."""
     cases = [(300, 270, 1000, "row", "row", 2, "f32", "bf16"), (257, 129, 777, "row", "col", 3, "bf16", "bf16"),
@@ -208,7 +216,7 @@ def test_split_k_deterministic_and_exact():
     oracle bit for bit and repeats bit for bit."""
     M, N, K = 384, 256, 3000
     A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", 3000, 256, "bf16", ("int", 4), ("int", 4), seed=8)
-    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=(128, 128, 64, 4, 4, 6))[0]
+    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=(128, 128, 64, 4, 4, 32, 0, 6))[0]
             for _ in range(2)]
     ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row")
     assert np.array_equal(outs[0], ref) and np.array_equal(outs[0], outs[1])
@@ -219,7 +227,7 @@ def test_conv_split_k():
     x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=41)
     for S in (2, 3):
         say(f"conv split-K S={S}")
-        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=(128, 128, 64, 4, 4, S))
+        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=(128, 128, 64, 4, 4, 32, 0, S))
         ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
         assert_close(y, ref, Sabs, "bf16", f"conv split {S}")
 

@@ -63,18 +63,29 @@ def b128_conflict_free(addrs):
     return True
 
 
+@pytest.mark.parametrize("mi", [32, 16])
 @pytest.mark.parametrize("cpr", [8, 4])
-def test_k_contiguous_fragment_reads_conflict_free(cpr):
-    """ds_read_b128 of a 32x32x16 operand fragment: lane l reads row base+l%32, logical chunk 2*kk + l/32."""
+def test_k_contiguous_fragment_reads_conflict_free(cpr, mi):
+    """ds_read_b128 of an operand fragment.  32x32x16: lane l reads row base+l%32, logical chunk 2*kk + l/32;
+    16x16x32: row base+l%16, chunk 4*kk + l/16 (base: any fragment origin in the tile)."""
     pitch = cpr * 16
-    for base in (0, 32, 64, 96, 128, 224):
-        for kk in range(cpr // 2):
+    nh = 64 // mi
+    for base in range(0, 256, mi):
+        for kk in range(cpr // nh):
             addrs = []
             for lane in range(64):
-                row = base + lane % 32
-                c = 2 * kk + lane // 32
+                row = base + lane % mi
+                c = nh * kk + lane // mi
                 addrs.append(row * pitch + chunk(1, cpr, row, c) * 16)
-            assert b128_conflict_free(addrs), (cpr, base, kk)
+            assert b128_conflict_free(addrs), (cpr, mi, base, kk)
+
+
+def test_old_k_maps_conflict_for_16x16x32():
+    """The earlier maps ((row&7)^((row>>3)&1) and (row>>2)&3) were conflict-free for 32x32x16 reads only: the
+    16x16x32 pattern must catch them."""
+    for cpr, f in ((8, lambda r: (r & 7) ^ ((r >> 3) & 1)), (4, lambda r: (r >> 2) & 3)):
+        addrs = [(lane % 16) * cpr * 16 + ((lane // 16) ^ f(lane % 16)) * 16 for lane in range(64)]
+        assert not b128_conflict_free(addrs)
 
 
 def test_bank_model_rejects_the_measured_conflicting_map():
@@ -84,27 +95,45 @@ def test_bank_model_rejects_the_measured_conflicting_map():
     assert not b128_conflict_free(addrs)
 
 
+@pytest.mark.parametrize("mi", [32, 16])
 @pytest.mark.parametrize("rows_elems", [256, 128])
-@pytest.mark.parametrize("window,group", [(256, 32)])
-def test_mn_contiguous_transposed_reads_conflict_free(rows_elems, window, group):
-    """ds_read_b64_tr_b16: in 16-lane group G, lane i reads k-row 8*(G//2) + 4*h + i//4 of the k-step and the
-    8 bytes at element column 32*blk + 16*(G%2) + 4*(i%4) of the wave's sub-tile."""
+def test_mn_contiguous_transposed_reads_conflict_free(rows_elems, mi):
+    """ds_read_b64_tr_b16 (32 lanes per phase, 8 bytes each): in 16-lane group G, lane i reads 8 bytes at
+    element column 4*(i%4) of its group's 16 columns, k-row i//4 of its group's 4 rows (plus 4 for the second
+    read h).  32x32x16: group G covers k-rows 8*(G//2) + 4*h .. of the 16-row k-step and columns 16*(G%2) ..
+    of the 32-column fragment; 16x16x32: k-rows 8*G + 4*h .. of the 32-row k-step, the fragment's 16 columns."""
+    window, group = 256, 32
     cpr = rows_elems // 8
     pitch = rows_elems * 2
-    for wave_off in range(0, rows_elems, 32):  # any 32-column block a wave's sub-tile can start at
-        for blk in range(1):
-            for kk in range(4):
-                for h in range(2):
-                    addrs = []
-                    for lane in range(64):
-                        G, i = lane // 16, lane % 16
-                        row = 16 * kk + 8 * (G // 2) + 4 * h + i // 4
-                        col = wave_off + 32 * blk + 16 * (G % 2) + 4 * (i % 4)
-                        c, within = col // 8, (col % 8) * 2
-                        addrs.append(row * pitch + chunk(0, cpr, row, c) * 16 + within)
-                    for g0 in range(0, 64, group):
-                        units = bank_units(addrs[g0:g0 + group], 8, window)
-                        assert len(set(units)) == group, (rows_elems, window, blk, kk, h, g0)
+    ks = 16 if mi == 32 else 32
+    for frag in range(0, rows_elems, mi):  # any fragment origin within the tile row
+        for kk in range(64 // ks):
+            for h in range(2):
+                addrs = []
+                for lane in range(64):
+                    G, i = lane // 16, lane % 16
+                    if mi == 32:
+                        row = ks * kk + 8 * (G // 2) + 4 * h + i // 4
+                        col = frag + 16 * (G % 2) + 4 * (i % 4)
+                    else:
+                        row = ks * kk + 8 * G + 4 * h + i // 4
+                        col = frag + 4 * (i % 4)
+                    c, within = col // 8, (col % 8) * 2
+                    addrs.append(row * pitch + chunk(0, cpr, row, c) * 16 + within)
+                for g0 in range(0, 64, group):
+                    units = bank_units(addrs[g0:g0 + group], 8, window)
+                    assert len(set(units)) == group, (rows_elems, mi, frag, kk, h, g0)
+
+
+def test_old_mn_map_conflicts_for_16x16x32():
+    """{0,6,12,10}[row&3] served 32x32x16 reads only: k-rows r and r+8 share a phase in the 16x16x32 pattern."""
+    old = lambda r: (0xAC60 >> ((r & 3) * 4)) & 0xF
+    addrs = []
+    for lane in range(32):
+        G, i = lane // 16, lane % 16
+        row, col = 8 * G + i // 4, 4 * (i % 4)
+        addrs.append(row * 512 + ((col // 8) ^ old(row)) * 16 + (col % 8) * 2)
+    assert len(set(bank_units(addrs, 8, 256))) < 32
 
 
 def test_unsupported_geometry():
