@@ -147,7 +147,8 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return IGC_ERR_MISALIGNED;
     if ((int64_t)N * H * W * C * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
     if ((inst->bn * Kg + inst->bk) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
-    if (P > 0x7fff || Q > 0x7fff || Kg > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+    // K indices (with the padding tiles past K) must stay below 2^31
+    if (P > 0x7fff || Q > 0x7fff || Kg > 0x7fff0000) return IGC_ERR_UNSUPPORTED;
 
     Params p = {};
     p.A = x;
@@ -179,6 +180,11 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     p.pw = pw;
     p.dh = dh;
     p.dw = dw;
+    p.conv_uniform = (C % inst->bk) == 0;
+    p.tpt = p.conv_uniform ? C / inst->bk : 1;
+    p.cin_magic = fastdiv_magic((uint32_t)C);
+    p.s_magic = fastdiv_magic((uint32_t)S);
+    p.tpt_magic = fastdiv_magic((uint32_t)p.tpt);
     return launch(pl, p, stream);
 }
 

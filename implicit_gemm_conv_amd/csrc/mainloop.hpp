@@ -44,6 +44,7 @@
 
 #include <type_traits>
 
+#include "fastdiv.hpp"
 #include "ring.hpp"
 
 namespace igc {
@@ -98,7 +99,16 @@ struct Params {
     int vec_ok;      // output rows allow 8/16-byte vector stores
     // convolution geometry (CONV instances only)
     int H, W, Cin, R, S, P, Q, sh, sw, ph, pw, dh, dw;
+    int conv_uniform;  // Cin % BK == 0: every K tile lies within one filter tap
+    int tpt;           // K tiles per filter tap (Cin / BK) when conv_uniform
+    uint32_t cin_magic, s_magic, tpt_magic;  // fastdiv multipliers for Cin, S and tpt
 };
+
+// Loop variants, chosen per call and compiled as separate loops so that none
+// carries a branch between its MFMAs: GEMM with K % 8 == 0 or convolution
+// whose channel tiles straddle filter taps (PLAIN), K % 8 != 0 (RAGGED),
+// convolution with whole filter taps per K tile (UNIFORM_TAP).
+enum LoopVariant : int { PLAIN = 0, UNIFORM_TAP = 1, RAGGED = 2 };
 
 // XOR swizzle of the 16-byte chunk index within a K-contiguous LDS row of CPR
 // chunks.  On gfx950 the LDS serves a 128-bit read 16 lanes at a time over its
@@ -256,8 +266,9 @@ struct DmaState {
 // ---------------------------------------------------------------------------
 // The kernel body.
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, int V>
 struct Mainloop {
+    static constexpr bool kRagged = V == RAGGED, kUniformTap = V == UNIFORM_TAP;
     using TA = typename C::TA;
     using TB = typename C::TB;
     static constexpr int BM = C::BM, BN = C::BN, BK = C::BK, D = C::D, KK = C::KK;
@@ -294,6 +305,9 @@ struct Mainloop {
         setup_dma();
         setup_frag_offsets();
         if constexpr (C::A_KC) ca_lane = TA::logical_chunk(wave, lane);
+        // every load of a lane sits 16*k rows below its first, and the K
+        // swizzle depends on row % 16 only: one logical chunk per lane
+        static_assert(!C::A_KC || (C::NW * TA::RPI) % 16 == 0, "a lane's A chunk must not change between its loads");
         if constexpr (C::B_KC) cb_lane = TB::logical_chunk(wave, lane);
     }
 
@@ -403,29 +417,32 @@ struct Mainloop {
         if constexpr (OP == 0 && J1 > J0) {
             if constexpr (C::CONV) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A);
-                const bool uniform_tap = (p.Cin % BK) == 0;
-                int r = 0, s = 0, cbase = 0;
-                if (uniform_tap) {
-                    const int tap = (int)(k0 / p.Cin);
-                    r = tap / p.S;
-                    s = tap - r * p.S;
-                    cbase = (int)(k0 - (int64_t)tap * p.Cin);
+                // K index k = ((r*S + s) * Cin + c): filter tap (r, s), channel c.
+                // This lane's chunk is the same logical chunk for all its loads.
+                int r, s, cin;
+                if constexpr (kUniformTap) {
+                    // the whole tile lies in one tap: scalar split of the tile index
+                    const uint32_t tg = (uint32_t)(k0 / BK);
+                    const uint32_t tap = fastdiv(tg, (uint32_t)p.tpt, p.tpt_magic);
+                    const uint32_t rr = fastdiv(tap, (uint32_t)p.S, p.s_magic);
+                    r = (int)rr;
+                    s = (int)(tap - rr * (uint32_t)p.S);
+                    cin = (int)(tg - tap * (uint32_t)p.tpt) * BK + 8 * ca_lane;
+                } else {
+                    const uint32_t kg = (uint32_t)k0 + 8u * (uint32_t)ca_lane;
+                    const uint32_t tap = fastdiv(kg, (uint32_t)p.Cin, p.cin_magic);
+                    const uint32_t rr = fastdiv(tap, (uint32_t)p.S, p.s_magic);
+                    r = (int)rr;
+                    s = (int)(tap - rr * (uint32_t)p.S);
+                    cin = (int)(kg - tap * (uint32_t)p.Cin);
                 }
+                const bool kok = 8 * ca_lane < krem;
+                const int dhr = r * p.dh, dws = s * p.dw;
                 static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     const int q = j * C::NW + wave;
-                    const int c = TA::logical_chunk(q, lane);
-                    int rr = r, ss = s, cin = cbase + 8 * c;
-                    bool kok = 8 * c < krem;
-                    if (!uniform_tap) {
-                        const int kg = (int)k0 + 8 * c;
-                        const int tap = kg / p.Cin;
-                        cin = kg - tap * p.Cin;
-                        rr = tap / p.S;
-                        ss = tap - rr * p.S;
-                    }
-                    const int h = conv_h0[j] + rr * p.dh;
-                    const int w = conv_w0[j] + ss * p.dw;
+                    const int h = conv_h0[j] + dhr;
+                    const int w = conv_w0[j] + dws;
                     const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
                     const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
                     dma16(rs, sa + q * 1024, ok ? off : kOob);
@@ -491,6 +508,7 @@ struct Mainloop {
     // when K % 8 != 0, the chunk straddling K holds elements k >= K read from
     // beyond the row's end; the lane that fetched it zeroes them.
     __device__ __forceinline__ void fixup_ragged_k(int t, IGC_LDS char* sa, IGC_LDS char* sb) {
+        if constexpr (!kRagged) return;
         const int64_t k0 = kbase + (int64_t)t * BK;
         if (!p.k_ragged8 || k0 + BK <= p.K) return;
         // the only chunk that straddles K is the one starting at k0 + 8*cs
@@ -573,15 +591,15 @@ struct Mainloop {
     // Wait until at most n later K tiles of this wave's loads are still in
     // flight (n in [0, D-2]); loads complete in issue order, so the oldest
     // outstanding tile has then landed.
-    template <int V>
+    template <int NMAX>
     __device__ __forceinline__ static void wait_tiles(int n) {
-        if constexpr (V <= 0) {
+        if constexpr (NMAX <= 0) {
             wait_vmcnt<0>();
         } else {
-            if (n >= V) {
-                wait_vmcnt<V * C::LPT>();
+            if (n >= NMAX) {
+                wait_vmcnt<NMAX * C::LPT>();
             } else {
-                wait_tiles<V - 1>(n);
+                wait_tiles<NMAX - 1>(n);
             }
         }
     }
@@ -703,18 +721,11 @@ __device__ __forceinline__ IGC_LDS char* slot_a() { return slot<C, Ring::slot_of
 template <class C, int u>
 __device__ __forceinline__ IGC_LDS char* slot_b() { return slot<C, Ring::slot_of(C::U, 2 * u + 1)>(); }
 
-template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
-    using ML = Mainloop<C>;
+// One output tile: setup, the K loop of variant V, epilogue.
+template <class C, int V>
+__device__ __forceinline__ void run_tile(const Params p, int split, int tm, int tn, int64_t kbase, int64_t kend) {
+    using ML = Mainloop<C, V>;
     constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN, U = C::U, P = C::P;
-
-    // workgroups s*T .. s*T+T-1 (T output tiles) take K split s
-    const int T = p.tiles_m * p.tiles_n;
-    const int split = (int)blockIdx.x / T;
-    int tm, tn;
-    tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int64_t kbase = (int64_t)split * p.k_per_split;
-    const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
     ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN, kbase, kend);
     const int KT = ml.KT, KTp = ml.KTp;
 
@@ -731,14 +742,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     // padded loop runs the same MFMA sequence, so no copies of them are needed.
     constexpr int NMF = FM * FN;
     constexpr int DSR = ML::DS_READS;
-    // The loop is compiled twice: with the K % 8 fixup between each tile's wait
-    // and barrier (RAGGED), and without it, so the common case carries no
-    // branch inside the loop.
-    auto kloop = [&](auto ragged) __attribute__((always_inline)) {
-    constexpr bool RAGGED = decltype(ragged)::value;
-    auto fixup = [&](int t, IGC_LDS char* sa, IGC_LDS char* sb) __attribute__((always_inline)) {
-        if constexpr (RAGGED) ml.fixup_ragged_k(t, sa, sb);
-    };
     if constexpr (C::SPREAD) {
         // ---- operand-slot ring (ring.hpp): unit s = operand s%2 of tile s/2 in
         // slot s % U.  Prologue: units 0 .. U-3; during tile t the units
@@ -750,7 +753,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
             ml.template issue_op<s % 2, 0, ML::template ipw<s % 2>()>(s / 2, slot<C, s>());
         });
         wait_vmcnt<WAITN>();
-        fixup(0, slot_a<C, 0>(), slot_b<C, 0>());
+        ml.fixup_ragged_k(0, slot_a<C, 0>(), slot_b<C, 0>());
         ring_barrier();
         ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
         for (int t0 = 0; t0 < KTp; t0 += P) {
@@ -778,7 +781,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
                 ml.template issue_units_part<KK - 1, KK, op1, op2>(t1, d1, t2, d2);
                 // ready(t+1) and free(t): the units newer than B(t+1) may stay in flight
                 wait_vmcnt<WAITN>();
-                fixup(t + 1, slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>());
+                ml.fixup_ragged_k(t + 1, slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>());
                 ring_barrier();
                 ml.read_frags(slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
                 ML::mma(acc, fa[pl], fb[pl]);
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
             if (S < KTp) ml.issue(S, slot_a<C, S>(), slot_b<C, S>());
         });
         ml.template wait_tiles<D - 1>(Ring::inflight_after(D, KTp, 0));
-        fixup(0, slot_a<C, 0>(), slot_b<C, 0>());
+        ml.fixup_ragged_k(0, slot_a<C, 0>(), slot_b<C, 0>());
         ring_barrier();
         ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
         // ---- steady state, unrolled by D so every slot is a constant
@@ -815,7 +818,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
                 // ready(t+1): own loads landed, then everyone; free(t): all reads of t done.
                 // After the last tile this is a harmless extra barrier and read.
                 ml.template wait_tiles<D - 2>(Ring::inflight_after(D, KTp, t + 1));
-                fixup(t + 1, slot_a<C, un>(), slot_b<C, un>());
+                ml.fixup_ragged_k(t + 1, slot_a<C, un>(), slot_b<C, un>());
                 ring_barrier();
                 if (t + D < KTp) ml.issue(t + D, slot_a<C, u>(), slot_b<C, u>());
                 ml.read_frags(slot_a<C, un>(), slot_b<C, un>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
@@ -830,7 +833,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
         IGC_LDS char* sb = slot_b<C, 0>();
         if (KT > 0) ml.issue(0, sa, sb);
         wait_vmcnt<0>();
-        fixup(0, sa, sb);
+        ml.fixup_ragged_k(0, sa, sb);
         ring_barrier();
         ml.read_frags(sa, sb, 0, fa[0], fb[0]);
         for (int t = 0; t < KT; ++t) {
@@ -843,26 +846,41 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
             ring_barrier();  // free: every wave has read tile t
             if (t + 1 < KT) ml.issue(t + 1, sa, sb);
             wait_vmcnt<0>();
-            fixup(t + 1, sa, sb);
+            ml.fixup_ragged_k(t + 1, sa, sb);
             ring_barrier();  // ready: tile t+1 landed for every wave
             ml.read_frags(sa, sb, 0, fa[0], fb[0]);
             ML::mma(acc, fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    };
-    if constexpr (C::CONV) {
-        kloop(std::false_type{});  // channels are a multiple of 8: never ragged
-    } else if (p.k_ragged8) {
-        kloop(std::true_type{});
-    } else {
-        kloop(std::false_type{});
-    }
     // ---- output epilogue: nothing is in flight any more
     if (p.k_splits > 1)
         ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
     else
         ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
+    // workgroups s*T .. s*T+T-1 (T output tiles) take K split s
+    const int T = p.tiles_m * p.tiles_n;
+    const int split = (int)blockIdx.x / T;
+    int tm, tn;
+    tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int64_t kbase = (int64_t)split * p.k_per_split;
+    const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
+    if constexpr (C::CONV) {
+        // channels are a multiple of 8, so K never is ragged
+        if (p.conv_uniform)
+            run_tile<C, UNIFORM_TAP>(p, split, tm, tn, kbase, kend);
+        else
+            run_tile<C, PLAIN>(p, split, tm, tn, kbase, kend);
+    } else {
+        if (p.k_ragged8)
+            run_tile<C, RAGGED>(p, split, tm, tn, kbase, kend);
+        else
+            run_tile<C, PLAIN>(p, split, tm, tn, kbase, kend);
+    }
 }
 
 }  // namespace igc

@@ -109,8 +109,9 @@ igc_status_t gemm_fp16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_
  *      P = (H + 2*ph - dh*(R-1) - 1)/sh + 1,  Q = (W + 2*pw - dw*(S-1) - 1)/sw + 1.
  * Requirements: N, H, W, C, K, R, S >= 1 (N or K may be 0: no-op), strides and
  * dilations >= 1, pads >= 0, P >= 1 and Q >= 1 (else IGC_ERR_INVALID_VALUE);
- * C % 8 == 0 (else IGC_ERR_MISALIGNED); x must span < 2^31 bytes (else
- * IGC_ERR_UNSUPPORTED).  The GEMM view is M = N*P*Q, N_gemm = K, K_gemm = R*S*C.
+ * C % 8 == 0 (else IGC_ERR_MISALIGNED); x must span < 2^31 bytes and
+ * R*S*C must not exceed 0x7fff0000 (else IGC_ERR_UNSUPPORTED).  The GEMM view
+ * is M = N*P*Q, N_gemm = K, K_gemm = R*S*C.
  */
 igc_status_t conv2d_nhwc_implicit_gemm(int N, int H, int W, int C, int K, int R, int S, int stride_h,
                                        int stride_w, int pad_h, int pad_w, int dil_h, int dil_w, const void *x,
