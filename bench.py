@@ -29,6 +29,9 @@ from implicit_gemm_conv_amd import inputs  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 flop/clk/CU x 2.4 GHz
 GEMM = "gemm_bf16_8192x8192x8192"
 CONV = "conv_bf16_n32_56x56_c256_k256_3x3"
+# HBM bytes per GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (copy-calibrated),
+# valid only for the kernel sources they were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_8192_traffic.txt")
 
 
 def log(*a):
@@ -48,6 +51,33 @@ def conv_geometry(c):
 def conv_flops(c):
     P, Q = conv_geometry(c)
     return 2.0 * c["N"] * P * Q * c["K"] * c["R"] * c["S"] * c["C"]
+
+
+def kernel_source_hash():
+    """Digest of the kernel sources and the ABI header: counter readings taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "implicit_gemm_conv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("probes"):
+            continue  # measurement kernels, not the GEMM
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "igc.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(tune):
+    """HBM bytes (fetch + write) per GEMM launch from the counter record, or None when the record is missing, was
+    taken on other kernel sources or another tile configuration."""
+    try:
+        rec = dict(line.strip().split("=", 1) for line in open(TRAFFIC_FILE) if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("tune") != tune:
+        return None
+    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
 def cpu_baseline(gcfg, ccfg, A, B, x, w):
@@ -165,6 +195,8 @@ def main():
     total_ms = evs[0][0].elapsed_time(evs[-1][2])
     ms_per_step = total_ms / args.steps
     gf, cf = gemm_flops(g), conv_flops(c)
+    t_used = igc.igc_default_tune(g["M"], g["N"], g["K"]) if gtune is None else igc.Tune(*gtune)
+    tune_str = ",".join(map(str, t_used.astuple()))
     value = (gf + cf) / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = gf / (gemm_ms.mean() * 1e-3) / 1e12
     conv_tflops = cf / (conv_ms.mean() * 1e-3) / 1e12
@@ -183,6 +215,12 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {n * 4} bytes read and written once")
         del src, dst
+
+    # MFMA-only ceiling with the same MFMA shape and wave count as the GEMM's tile (untimed)
+    from implicit_gemm_conv_amd import probes
+    ceiling = probes.mfma_ceiling(t_used.mfma or 32, t_used.waves)
+    ceiling["gemm_frac_of_ceiling"] = round(gemm_tflops / ceiling["tflops"], 4)
+    log(f"MFMA-only ceiling: {ceiling}")
 
     base = None
     if not args.no_cpu_baseline:
@@ -210,8 +248,10 @@ def main():
         "kernels": {"gemm_us": round(float(gemm_ms.mean() * 1e3), 2), "gemm_tflops": round(gemm_tflops, 1),
                     "conv_us": round(float(conv_ms.mean() * 1e3), 2), "conv_tflops": round(conv_tflops, 1)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_kernel (8192^3 bf16)"},
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(tune_str),
+                     "kernel": f"gemm_kernel (8192^3 bf16, tile {tune_str})"},
+        "mfma_ceiling": ceiling,
         "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)

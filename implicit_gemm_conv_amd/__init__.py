@@ -73,6 +73,10 @@ def lib():
         L.igc_status_string.restype = ctypes.c_char_p
         L.igc_ring_schedule.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_int), i32]
         L.igc_ring_schedule.restype = i32
+        L.igc_probe_mfma.argtypes = [i32, i32, i32, i32, p, i64, p, i64, p]
+        L.igc_probe_mfma.restype = i32
+        L.igc_probe_dma.argtypes = [i32, i32, p, p, i64, p, i64, p]
+        L.igc_probe_dma.restype = i32
         _lib = L
     return _lib
 
@@ -184,6 +188,15 @@ def igc_ring_schedule(pipe_depth, k_tiles, half_stage=0):
     buf = (ctypes.c_int * (4 * max(n, 1)))()
     lib().igc_ring_schedule(pipe_depth, half_stage, k_tiles, buf, n)
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def igc_probe_mfma(mfma, waves, iters, grid, sink, sink_bytes, clk, clk_bytes, stream=None):
+    return lib().igc_probe_mfma(mfma, waves, iters, grid, _ptr(sink), sink_bytes, _ptr(clk), clk_bytes,
+                                _stream(stream))
+
+
+def igc_probe_dma(bk, operands, A, B, bytes_each, clk, clk_bytes, stream=None):
+    return lib().igc_probe_dma(bk, operands, _ptr(A), _ptr(B), bytes_each, _ptr(clk), clk_bytes, _stream(stream))
 
 
 def check(status):

@@ -2,7 +2,8 @@
 
 Each tile configuration listed in csrc/tile_configs.hpp is compiled as its own
 object from csrc/instances.hip (in parallel), then linked with the host-side
-C ABI (csrc/igc_lib.hip, csrc/registry.hip).
+C ABI (csrc/igc_lib.hip, csrc/registry.hip), the split-K reduction
+(csrc/split_reduce.hip) and the measurement probes (csrc/probes.hip).
 """
 import concurrent.futures
 import os
@@ -45,7 +46,7 @@ def build(jobs=None, verbose=False):
         obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}.o")
         units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}", f"-DIGC_W={w}",
                       f"-DIGC_MI={mi}", f"-DIGC_HALF={h}", "-c", os.path.join(CSRC, "instances.hip"), "-o", obj])
-    for name in ("igc_lib", "registry", "split_reduce"):
+    for name in ("igc_lib", "registry", "split_reduce", "probes"):
         units.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, name + ".hip"),
                       "-o", os.path.join(OBJ_DIR, name + ".o")])
     jobs = jobs or min(len(units), max(1, (os.cpu_count() or 4)))

@@ -95,6 +95,41 @@ def test_conv_validation(args, expect):
     assert st == expect, igc.igc_status_string(st)
 
 
+@pytest.mark.parametrize("args,expect", [
+    (dict(mfma=8), igc.IGC_ERR_INVALID_VALUE),
+    (dict(waves=6), igc.IGC_ERR_INVALID_VALUE),
+    (dict(iters=0), igc.IGC_ERR_INVALID_VALUE),
+    (dict(grid=0), igc.IGC_ERR_INVALID_VALUE),
+    (dict(sink_bytes=512 * 8 * 64 * 4 - 4), igc.IGC_ERR_INVALID_VALUE),  # one float short
+    (dict(clk_bytes=512 * 8 - 4), igc.IGC_ERR_INVALID_VALUE),
+    (dict(sink=None), igc.IGC_ERR_INVALID_VALUE),
+    (dict(sink=FAKE + 2), igc.IGC_ERR_MISALIGNED),
+])
+def test_probe_mfma_validation(args, expect):
+    a = dict(mfma=16, waves=8, iters=10, grid=512, sink=FAKE, sink_bytes=512 * 8 * 64 * 4, clk=FAKE,
+             clk_bytes=512 * 8)
+    a.update(args)
+    st = igc.igc_probe_mfma(a["mfma"], a["waves"], a["iters"], a["grid"], a["sink"], a["sink_bytes"], a["clk"],
+                            a["clk_bytes"], stream=0)
+    assert st == expect, igc.igc_status_string(st)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(bk=48), igc.IGC_ERR_INVALID_VALUE),
+    (dict(operands=0), igc.IGC_ERR_INVALID_VALUE),
+    (dict(operands=4), igc.IGC_ERR_INVALID_VALUE),
+    (dict(bytes_each=8192 * 8192 * 2 - 2), igc.IGC_ERR_INVALID_VALUE),  # must hold an 8192^2 bf16 matrix
+    (dict(clk_bytes=1024 * 8 - 4), igc.IGC_ERR_INVALID_VALUE),
+    (dict(A=FAKE + 8), igc.IGC_ERR_MISALIGNED),
+])
+def test_probe_dma_validation(args, expect):
+    a = dict(bk=32, operands=3, A=FAKE, B=FAKE, bytes_each=8192 * 8192 * 2, clk=FAKE, clk_bytes=1024 * 8)
+    a.update(args)
+    st = igc.igc_probe_dma(a["bk"], a["operands"], a["A"], a["B"], a["bytes_each"], a["clk"], a["clk_bytes"],
+                           stream=0)
+    assert st == expect, igc.igc_status_string(st)
+
+
 def test_tune_table_fits_lds():
     """Every compiled ring fits the 160 KB of LDS of one CU (a stage costs (BM+BN)*BK*2 bytes)."""
     tunes = igc.tunes()
