@@ -30,11 +30,12 @@ class IgcError(RuntimeError):
 class Tune(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int), ("pipe_depth", ctypes.c_int),
                 ("waves", ctypes.c_int), ("mfma", ctypes.c_int), ("half_stage", ctypes.c_int),
-                ("k_splits", ctypes.c_int)]
+                ("loader_waves", ctypes.c_int), ("k_splits", ctypes.c_int), ("stream_k", ctypes.c_int)]
 
     def astuple(self):
-        """(bm, bn, bk, pipe_depth, waves, mfma, half_stage): the compiled configuration."""
-        return (self.bm, self.bn, self.bk, self.pipe_depth, self.waves, self.mfma or 32, self.half_stage)
+        """(bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves): the compiled configuration."""
+        return (self.bm, self.bn, self.bk, self.pipe_depth, self.waves, self.mfma or 32, self.half_stage,
+                self.loader_waves or self.waves)
 
 
 _lib = None
@@ -169,7 +170,7 @@ def igc_tune_lds_bytes(tune):
 
 
 def tunes():
-    """All compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage) configurations."""
+    """All compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves) configurations."""
     return [igc_tune_get(i).astuple() for i in range(igc_tune_count())]
 
 

@@ -28,7 +28,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-
 def tile_configs():
     text = open(os.path.join(CSRC, "tile_configs.hpp")).read()
     return [tuple(int(v) for v in m)
-            for m in re.findall(r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", text)]
+            for m in re.findall(r"X\((\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\)", text)]
 
 
 def _run(cmd):
@@ -42,10 +42,11 @@ def _run(cmd):
 def build(jobs=None, verbose=False):
     os.makedirs(OBJ_DIR, exist_ok=True)
     units = []
-    for (bm, bn, bk, d, w, mi, h) in tile_configs():
-        obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}.o")
+    for (bm, bn, bk, d, w, mi, h, lw) in tile_configs():
+        obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}x{lw}.o")
         units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}", f"-DIGC_W={w}",
-                      f"-DIGC_MI={mi}", f"-DIGC_HALF={h}", "-c", os.path.join(CSRC, "instances.hip"), "-o", obj])
+                      f"-DIGC_MI={mi}", f"-DIGC_HALF={h}", f"-DIGC_LW={lw}", "-c", os.path.join(CSRC, "instances.hip"),
+                      "-o", obj])
     for name in ("igc_lib", "registry", "split_reduce", "probes"):
         units.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, name + ".hip"),
                       "-o", os.path.join(OBJ_DIR, name + ".o")])

@@ -28,6 +28,8 @@ static int out_size(igc_out_t t) { return t == IGC_OUT_F32 ? 4 : 2; }
 struct Plan {
     const Instance* inst = nullptr;
     int splits = 1;
+    int stream_k = 0;  // persistent workgroups of a stream-K schedule (0: none)
+    bool valid = true;
 };
 
 // The tile configuration and K split for one call: an explicit tune is taken as
@@ -38,6 +40,8 @@ static Plan pick(const igc_tune_t* tune, bool fp16, bool a_kc, bool b_kc, bool c
     Plan pl;
     pl.inst = find_instance(t, fp16, a_kc, b_kc, conv);
     pl.splits = t.k_splits > 1 ? t.k_splits : 1;
+    pl.stream_k = t.stream_k > 0 ? t.stream_k : 0;
+    pl.valid = t.stream_k >= 0 && !(pl.splits > 1 && pl.stream_k > 0);
     return pl;
 }
 
@@ -49,6 +53,30 @@ static igc_status_t launch(const Plan& pl, Params p, hipStream_t stream) {
     const Instance* inst = pl.inst;
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     if (tiles <= 0) return IGC_OK;
+    if (pl.stream_k > 0 && p.K > 0) {
+        // stream-K: K of every tile in units of one ring period; G runs of equal length
+        const int64_t unit = (int64_t)inst->bk * Ring::period(Ring::units(inst->d, inst->half));
+        const int64_t UT = (p.K + unit - 1) / unit;
+        const int64_t G = pl.stream_k < tiles * UT ? pl.stream_k : tiles * UT;
+        const size_t part_bytes = (size_t)G * inst->bm * inst->bn * sizeof(float);
+        char* ws = nullptr;
+        (void)hipGetLastError();
+        if (hipMallocAsync((void**)&ws, part_bytes + (size_t)G * sizeof(int), stream) != hipSuccess)
+            return IGC_ERR_HIP;
+        p.sk_grid = (int)G;
+        p.sk_units = UT;
+        p.sk_ws = (float*)ws;
+        p.sk_flags = (int*)(ws + part_bytes);
+        p.k_splits = 1;
+        hipError_t e = hipMemsetAsync(p.sk_flags, 0, (size_t)G * sizeof(int), stream);
+        Params arg = p;
+        void* args[] = {&arg};
+        if (e == hipSuccess)
+            e = hipLaunchKernel(inst->fn, dim3((unsigned)G), dim3(64 * inst->waves), args, 0, stream);
+        (void)hipFreeAsync(ws, stream);
+        if (e != hipSuccess) return IGC_ERR_HIP;
+        return hipGetLastError() == hipSuccess ? IGC_OK : IGC_ERR_HIP;
+    }
     int S = 1;
     p.k_per_split = p.K > 0 ? p.K : 1;
     if (pl.splits > 1 && p.K > 0) {
@@ -88,6 +116,7 @@ static igc_status_t gemm_any(bool fp16, int64_t M, int64_t N, int64_t K, const v
     if (ct != IGC_OUT_F32 && ct != IGC_OUT_BF16 && ct != IGC_OUT_F16) return IGC_ERR_INVALID_VALUE;
     const bool a_kc = la == IGC_ROW_MAJOR, b_kc = lb == IGC_COL_MAJOR;
     const Plan pl = pick(tune, fp16, a_kc, b_kc, false, M, N, K);
+    if (!pl.valid) return IGC_ERR_INVALID_VALUE;
     const Instance* inst = pl.inst;
     if (!inst) return IGC_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return IGC_OK;
@@ -139,6 +168,7 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     const int64_t P = hspan / sh + 1, Q = wspan / sw + 1;
     const int64_t Mg = (int64_t)N * P * Q, Ng = K, Kg = (int64_t)R * S * C;
     const Plan pl = pick(tune, fp16, true, true, true, Mg, Ng, Kg);
+    if (!pl.valid) return IGC_ERR_INVALID_VALUE;
     const Instance* inst = pl.inst;
     if (!inst) return IGC_ERR_UNSUPPORTED;
     if (Mg == 0 || Ng == 0) return IGC_OK;

@@ -8,15 +8,15 @@
 namespace igc {
 
 struct Instance {
-    int bm, bn, bk, d, waves, mfma, half;
+    int bm, bn, bk, d, waves, mfma, half, loaders;
     bool fp16, a_kc, b_kc, conv;
     const void* fn;      // __global__ gemm_kernel<Cfg<...>>
     int64_t lds_bytes;   // static LDS of one workgroup
 };
 
 // One table per tile configuration, defined in instances.hip.
-#define IGC_DECLARE_TABLE(BM, BN, BK, D, W, MI, H) \
-    const Instance* instance_table_##BM##x##BN##x##BK##x##D##x##W##x##MI##x##H(int* count);
+#define IGC_DECLARE_TABLE(BM, BN, BK, D, W, MI, H, L) \
+    const Instance* instance_table_##BM##x##BN##x##BK##x##D##x##W##x##MI##x##H##x##L(int* count);
 IGC_FOR_EACH_TILE(IGC_DECLARE_TABLE)
 #undef IGC_DECLARE_TABLE
 

@@ -99,6 +99,16 @@ struct Params {
     int vec_ok;      // output rows allow 8/16-byte vector stores
     // convolution geometry (CONV instances only)
     int H, W, Cin, R, S, P, Q, sh, sw, ph, pw, dh, dw;
+    // stream-K (sk_grid > 0 workgroups): the tiles' K ranges, in units of the
+    // ring period (sk_units per tile), are cut into sk_grid equal runs; a
+    // workgroup whose run ends inside a tile publishes an fp32 partial tile in
+    // sk_ws (one BM x BN slot per workgroup) and raises sk_flags[its index];
+    // the workgroup that computes the tile's last K unit adds the partials of
+    // the lower workgroups in descending order and stores the tile.
+    int sk_grid;
+    int64_t sk_units;
+    float* sk_ws;
+    int* sk_flags;
     int conv_uniform;  // Cin % BK == 0: every K tile lies within one filter tap
     int tpt;           // K tiles per filter tap (Cin / BK) when conv_uniform
     uint32_t cin_magic, s_magic, tpt_magic;  // fastdiv multipliers for Cin, S and tpt
@@ -177,15 +187,15 @@ __device__ __forceinline__ f32x4_t mfma(i16x8_t a, i16x8_t b, f32x4_t c) {
 //   KC = true : LDS tile is ROWS rows of BK elements (K contiguous).
 //   KC = false: LDS tile is BK rows of ROWS elements (M or N contiguous).
 // ---------------------------------------------------------------------------
-template <int ROWS, int BK, bool KC, int NW>
+template <int ROWS, int BK, bool KC, int NL>
 struct Tile {
     static constexpr int BYTES = ROWS * BK * 2;
     static constexpr int INSTR = BYTES / 1024;        // 1 KB wave instructions per stage
-    static constexpr int IPW = INSTR / NW;            // per wave
+    static constexpr int IPW = INSTR / NL;            // per loading wave
     static constexpr int ROW_ELEMS = KC ? BK : ROWS;  // elements per LDS row
     static constexpr int CPR = ROW_ELEMS / 8;         // 16-byte chunks per LDS row
     static constexpr int RPI = 64 / CPR;              // LDS rows per wave instruction
-    static_assert(BYTES % (1024 * NW) == 0, "tile must split into whole wave instructions");
+    static_assert(BYTES % (1024 * NL) == 0, "tile must split into whole wave instructions");
     static_assert(CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row must be 8..512 elements");
     // LDS row, physical chunk and logical chunk written by `lane` in wave instruction q.
     __device__ static int row_of(int q, int lane) { return q * RPI + lane / CPR; }
@@ -199,8 +209,8 @@ struct Tile {
     }
 };
 
-template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, int MI_, int HALF_, bool A_KC_, bool B_KC_,
-          bool CONV_>
+template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, int MI_, int HALF_, int NL_, bool A_KC_,
+          bool B_KC_, bool CONV_>
 struct Cfg {
     static constexpr bool FP16 = FP16_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, D = D_;
@@ -219,6 +229,12 @@ struct Cfg {
     // matrix core busy.
     static constexpr int NW = NW_, NT = 64 * NW_;
     static constexpr int WM = 2, WN = NW_ / 2;
+    // NL loading waves (0: all) issue every global->LDS load of a tile (waves
+    // 0 .. NL-1, one per SIMD when NL = 4 of 8); the others only read LDS and
+    // run MFMAs, so a SIMD always has a wave whose MFMA issue never waits
+    // behind the load path.
+    static constexpr int NL = NL_ == 0 ? NW_ : NL_;
+    static_assert(NL >= 1 && NL <= NW_ && NW_ % NL == 0, "loading waves divide the workgroup");
     // SPREAD: the two operand slots freed at the barrier before tile t are
     // refilled by loads interleaved through tile t's k-steps, instead of one
     // burst after the barrier.
@@ -230,8 +246,8 @@ struct Cfg {
     static constexpr int FM = WTM / MI, FN = WTN / MI;
     static constexpr int KK = BK / KS;                // MFMA k-steps per K tile
     static_assert(KK >= 1 && BK % KS == 0, "K tile is whole k-steps");
-    using TA = Tile<BM, BK, A_KC, NW>;
-    using TB = Tile<BN, BK, B_KC, NW>;
+    using TA = Tile<BM, BK, A_KC, NL>;
+    using TB = Tile<BN, BK, B_KC, NL>;
     // Slot s holds A units when s is even and U is even, B units when s is
     // odd and U is even; with U odd both operands rotate through every slot.
     static constexpr int SLOT_A = TA::BYTES, SLOT_B = TB::BYTES;
@@ -266,9 +282,10 @@ struct DmaState {
 // ---------------------------------------------------------------------------
 // The kernel body.
 // ---------------------------------------------------------------------------
-template <class C, int V>
+template <class C, int V, bool LOADER = true>
 struct Mainloop {
     static constexpr bool kRagged = V == RAGGED, kUniformTap = V == UNIFORM_TAP;
+    // LOADER: this wave issues global->LDS loads (waves 0 .. NL-1)
     using TA = typename C::TA;
     using TB = typename C::TB;
     static constexpr int BM = C::BM, BN = C::BN, BK = C::BK, D = C::D, KK = C::KK;
@@ -307,7 +324,7 @@ struct Mainloop {
         if constexpr (C::A_KC) ca_lane = TA::logical_chunk(wave, lane);
         // every load of a lane sits 16*k rows below its first, and the K
         // swizzle depends on row % 16 only: one logical chunk per lane
-        static_assert(!C::A_KC || (C::NW * TA::RPI) % 16 == 0, "a lane's A chunk must not change between its loads");
+        static_assert(!C::A_KC || (C::NL * TA::RPI) % 16 == 0, "a lane's A chunk must not change between its loads");
         if constexpr (C::B_KC) cb_lane = TB::logical_chunk(wave, lane);
     }
 
@@ -315,7 +332,7 @@ struct Mainloop {
         // Operand A
 #pragma unroll
         for (int j = 0; j < TA::IPW; ++j) {
-            const int q = j * C::NW + wave;
+            const int q = j * C::NL + wave;
             const int row = TA::row_of(q, lane);
             const int c = TA::logical_chunk(q, lane);
             if constexpr (C::CONV) {
@@ -341,7 +358,7 @@ struct Mainloop {
         // Operand B
 #pragma unroll
         for (int j = 0; j < TB::IPW; ++j) {
-            const int q = j * C::NW + wave;
+            const int q = j * C::NL + wave;
             const int row = TB::row_of(q, lane);
             const int c = TB::logical_chunk(q, lane);
             if constexpr (C::B_KC) {
@@ -406,6 +423,7 @@ struct Mainloop {
     // operand, so one compare per tile does.
     template <int OP, int J0, int J1>
     __device__ __forceinline__ void issue_op(int t, IGC_LDS char* dst) {
+        if constexpr (!LOADER) return;
         const int64_t k0 = kbase + (int64_t)t * BK;
         IGC_LDS char* sa = dst;
         IGC_LDS char* sb = dst;
@@ -440,7 +458,7 @@ struct Mainloop {
                 const int dhr = r * p.dh, dws = s * p.dw;
                 static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
-                    const int q = j * C::NW + wave;
+                    const int q = j * C::NL + wave;
                     const int h = conv_h0[j] + dhr;
                     const int w = conv_w0[j] + dws;
                     const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
@@ -452,13 +470,13 @@ struct Mainloop {
                 const bool kout = 8 * ca_lane >= krem;
                 static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
-                    dma16(rs, sa + (j * C::NW + wave) * 1024, kout ? kOob : da.voff[j]);
+                    dma16(rs, sa + (j * C::NL + wave) * 1024, kout ? kOob : da.voff[j]);
                 });
             } else {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (k0 * p.lda + m0) * 2);
                 static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
-                    const int q = j * C::NW + wave;
+                    const int q = j * C::NL + wave;
                     dma16(rs, sa + q * 1024, TA::row_of(q, lane) >= krem ? kOob : da.voff[j]);
                 });
             }
@@ -471,13 +489,13 @@ struct Mainloop {
                 const bool kout = 8 * cb_lane >= krem;
                 static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
-                    dma16(rs, sb + (j * C::NW + wave) * 1024, kout ? kOob : db.voff[j]);
+                    dma16(rs, sb + (j * C::NL + wave) * 1024, kout ? kOob : db.voff[j]);
                 });
             } else {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (k0 * p.ldb + n0) * 2);
                 static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
-                    const int q = j * C::NW + wave;
+                    const int q = j * C::NL + wave;
                     dma16(rs, sb + q * 1024, TB::row_of(q, lane) >= krem ? kOob : db.voff[j]);
                 });
             }
@@ -508,7 +526,7 @@ struct Mainloop {
     // when K % 8 != 0, the chunk straddling K holds elements k >= K read from
     // beyond the row's end; the lane that fetched it zeroes them.
     __device__ __forceinline__ void fixup_ragged_k(int t, IGC_LDS char* sa, IGC_LDS char* sb) {
-        if constexpr (!kRagged) return;
+        if constexpr (!kRagged || !LOADER) return;
         const int64_t k0 = kbase + (int64_t)t * BK;
         if (!p.k_ragged8 || k0 + BK <= p.K) return;
         // the only chunk that straddles K is the one starting at k0 + 8*cs
@@ -534,14 +552,14 @@ struct Mainloop {
         if constexpr (C::A_KC && !C::CONV) {
 #pragma unroll
             for (int j = 0; j < TA::IPW; ++j) {
-                const int q = j * C::NW + wave;
+                const int q = j * C::NL + wave;
                 fix(sa, q, TA::logical_chunk(q, lane));
             }
         }
         if constexpr (C::B_KC) {
 #pragma unroll
             for (int j = 0; j < TB::IPW; ++j) {
-                const int q = j * C::NW + wave;
+                const int q = j * C::NL + wave;
                 fix(sb, q, TB::logical_chunk(q, lane));
             }
         }
@@ -602,6 +620,71 @@ struct Mainloop {
                 wait_tiles<NMAX - 1>(n);
             }
         }
+    }
+
+    // ---- stream-K partial tiles ----------------------------------------------
+    // A partial tile is kept in lane order: 16-byte piece c of accumulator
+    // block (i, j) of wave w lies at float4 index ((w*FM + i)*FN + j)*NQ + c,
+    // times 64, plus the lane, so every store and load is one coalesced 1 KB
+    // wave access.
+    static constexpr int NQ = (int)(sizeof(Acc) / 16);
+    static_assert(C::NT / 64 * FM * FN * NQ * 64 * 4 == BM * BN, "partial tile holds BM x BN floats");
+
+    // Partial tiles and flags move with system-coherent buffer accesses (SC0 and
+    // SC1 set: stores write through to memory, loads do not hit stale cache
+    // lines), so workgroups on different XCDs exchange them without flushing
+    // or invalidating the caches other workgroups are using.
+    static constexpr int kCoherent = 1 | 16;             // SC0 | SC1
+    static constexpr int kCoherentVolatile = kCoherent | (1 << 31);
+
+    // Writes the partial tile, waits until this wave's stores are complete,
+    // and (once every wave is there) raises the flag.
+    __device__ __forceinline__ void sk_publish(const Acc (&acc)[FM][FN], float* part, int* flag) {
+        typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(part);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const f32x4_t v{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+                    const int off = ((((wave * FM + i) * FN + j) * NQ + c) * 64 + lane) * 16;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), rs, off, 0, kCoherent);
+                }
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(flag), 0, 0, kCoherent);
+    }
+
+    // Waits for a lower workgroup's flag (bounded: every wave leaves the loop
+    // even if the flag never rises) and adds its partial tile.
+    __device__ __forceinline__ void sk_collect(Acc (&acc)[FM][FN], const float* part, int* flag) {
+        typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+        if (threadIdx.x == 0) {
+            const __amdgpu_buffer_rsrc_t rf = make_rsrc(flag);
+            for (int spins = 0; spins < (1 << 24); ++spins) {
+                if (__builtin_amdgcn_raw_buffer_load_b32(rf, 0, 0, kCoherentVolatile) != 0) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(part);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const int off = ((((wave * FM + i) * FN + j) * NQ + c) * 64 + lane) * 16;
+                    const f32x4_t v = __builtin_bit_cast(
+                        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherentVolatile));
+                    acc[i][j][4 * c] += v[0];
+                    acc[i][j][4 * c + 1] += v[1];
+                    acc[i][j][4 * c + 2] += v[2];
+                    acc[i][j][4 * c + 3] += v[3];
+                }
     }
 
     // ---- epilogue: accumulators -> C ---------------------------------------
@@ -721,10 +804,28 @@ __device__ __forceinline__ IGC_LDS char* slot_a() { return slot<C, Ring::slot_of
 template <class C, int u>
 __device__ __forceinline__ IGC_LDS char* slot_b() { return slot<C, Ring::slot_of(C::U, 2 * u + 1)>(); }
 
-// One output tile: setup, the K loop of variant V, epilogue.
-template <class C, int V>
-__device__ __forceinline__ void run_tile(const Params p, int split, int tm, int tn, int64_t kbase, int64_t kend) {
-    using ML = Mainloop<C, V>;
+// The K range [kbase, kend) of one output tile: setup, the K loop of variant
+// V, then epi(ml, acc) with the accumulators.
+template <class C, int V, bool LOADER, class Epi>
+__device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int64_t kbase, int64_t kend, Epi&& epi);
+
+template <class C, int V, class Epi>
+__device__ __forceinline__ void run_tile(const Params p, int tm, int tn, int64_t kbase, int64_t kend, Epi&& epi) {
+    if constexpr (C::NL == C::NW) {
+        run_tile_as<C, V, true>(p, tm, tn, kbase, kend, epi);
+    } else {
+        // loading and compute-only waves run separately compiled copies of the
+        // same loop (identical barrier sequences), so neither has a branch in it
+        if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < C::NL)
+            run_tile_as<C, V, true>(p, tm, tn, kbase, kend, epi);
+        else
+            run_tile_as<C, V, false>(p, tm, tn, kbase, kend, epi);
+    }
+}
+
+template <class C, int V, bool LOADER, class Epi>
+__device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int64_t kbase, int64_t kend, Epi&& epi) {
+    using ML = Mainloop<C, V, LOADER>;
     constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN, U = C::U, P = C::P;
     ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN, kbase, kend);
     const int KT = ml.KT, KTp = ml.KTp;
@@ -854,14 +955,85 @@ __device__ __forceinline__ void run_tile(const Params p, int split, int tm, int 
         }
     }
     // ---- output epilogue: nothing is in flight any more
-    if (p.k_splits > 1)
-        ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
-    else
-        ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+    epi(ml, acc);
+}
+
+// Calls f(variant) with the loop variant this call needs, as a constant.
+template <class C, class F>
+__device__ __forceinline__ void with_variant(const Params p, F&& f) {
+    if constexpr (C::CONV) {
+        // channels are a multiple of 8, so K never is ragged
+        if (p.conv_uniform)
+            f(std::integral_constant<int, UNIFORM_TAP>{});
+        else
+            f(std::integral_constant<int, PLAIN>{});
+    } else {
+        if (p.k_ragged8)
+            f(std::integral_constant<int, RAGGED>{});
+        else
+            f(std::integral_constant<int, PLAIN>{});
+    }
+}
+
+// End (exclusive) of stream-K workgroup g's run of K units.
+__device__ __forceinline__ int64_t sk_end(int64_t total, int G, int g) { return total * (g + 1) / G; }
+
+// Stream-K: workgroup g takes the K units [b, e) of the tiles' concatenated K
+// ranges and walks them backwards, one tile segment at a time, so that it
+// first finishes the segment it shares with higher workgroups (publishing a
+// partial) and last the segment whose tile it owns (collecting the partials of
+// lower workgroups, which published theirs first).  An owner therefore only
+// waits on workgroups dispatched no later than itself.
+template <class C>
+__device__ __forceinline__ void stream_k(const Params p) {
+    constexpr int UNIT = C::P * C::BK;  // K elements per unit (one ring period)
+    const int G = p.sk_grid, g = (int)blockIdx.x;
+    const int64_t UT = p.sk_units;
+    const int64_t total = (int64_t)p.tiles_m * p.tiles_n * UT;
+    const int64_t b = total * g / G;
+    int64_t hi = sk_end(total, G, g);
+    while (hi > b) {
+        const int64_t tau = (hi - 1) / UT;
+        const int64_t lo = b > tau * UT ? b : tau * UT;
+        const int64_t u0 = lo - tau * UT, u1 = hi - tau * UT;
+        // When every run holds whole tiles (c of them), the j-th tile of every
+        // run is processed at the same time: give it the tile the
+        // data-parallel grid runs in round j on the same XCD, keeping that
+        // grid's L2 grouping.
+        const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
+        int64_t block = tau;
+        if (T % G == 0 && (total / G) % UT == 0) {
+            const int64_t c = T / G;
+            block = (tau % c) * G + tau / c;
+        }
+        int tm, tn;
+        tile_coords((int)block, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        const int64_t kbase = u0 * UNIT;
+        const int64_t kend = u1 * UNIT < p.K ? u1 * UNIT : p.K;
+        with_variant<C>(p, [&](auto v) __attribute__((always_inline)) {
+            run_tile<C, decltype(v)::value>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
+                if (u1 < UT) {
+                    ml.sk_publish(acc, p.sk_ws + (int64_t)g * (C::BM * C::BN), p.sk_flags + g);
+                } else {
+                    // owner: add the partials of the lower workgroups sharing this tile
+                    const int64_t tile_start = tau * UT;
+                    for (int gp = g - 1; gp >= 0 && sk_end(total, G, gp) > tile_start; --gp)
+                        ml.sk_collect(acc, p.sk_ws + (int64_t)gp * (C::BM * C::BN), p.sk_flags + gp);
+                    ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+                }
+            });
+        });
+        hi = lo;
+        __syncthreads();  // every wave is past this segment's LDS before the next prologue
+    }
 }
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
+    if (p.sk_grid > 0) {
+        stream_k<C>(p);
+        return;
+    }
     // workgroups s*T .. s*T+T-1 (T output tiles) take K split s
     const int T = p.tiles_m * p.tiles_n;
     const int split = (int)blockIdx.x / T;
@@ -869,18 +1041,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int64_t kbase = (int64_t)split * p.k_per_split;
     const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
-    if constexpr (C::CONV) {
-        // channels are a multiple of 8, so K never is ragged
-        if (p.conv_uniform)
-            run_tile<C, UNIFORM_TAP>(p, split, tm, tn, kbase, kend);
-        else
-            run_tile<C, PLAIN>(p, split, tm, tn, kbase, kend);
-    } else {
-        if (p.k_ragged8)
-            run_tile<C, RAGGED>(p, split, tm, tn, kbase, kend);
-        else
-            run_tile<C, PLAIN>(p, split, tm, tn, kbase, kend);
-    }
+    with_variant<C>(p, [&](auto v) __attribute__((always_inline)) {
+        run_tile<C, decltype(v)::value>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
+            if (p.k_splits > 1)
+                ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
+            else
+                ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+        });
+    });
 }
 
 }  // namespace igc

@@ -4,14 +4,14 @@
 namespace igc {
 
 static const igc_tune_t kTunes[] = {
-#define IGC_TUNE_ENTRY(BM, BN, BK, D, W, MI, H) {BM, BN, BK, D, W, MI, H, 0},
+#define IGC_TUNE_ENTRY(BM, BN, BK, D, W, MI, H, L) {BM, BN, BK, D, W, MI, H, L == 0 ? W : L, 0, 0},
     IGC_FOR_EACH_TILE(IGC_TUNE_ENTRY)
 #undef IGC_TUNE_ENTRY
 };
 
 typedef const Instance* (*TableFn)(int*);
 static const TableFn kTables[] = {
-#define IGC_TABLE_ENTRY(BM, BN, BK, D, W, MI, H) &instance_table_##BM##x##BN##x##BK##x##D##x##W##x##MI##x##H,
+#define IGC_TABLE_ENTRY(BM, BN, BK, D, W, MI, H, L) &instance_table_##BM##x##BN##x##BK##x##D##x##W##x##MI##x##H##x##L,
     IGC_FOR_EACH_TILE(IGC_TABLE_ENTRY)
 #undef IGC_TABLE_ENTRY
 };
@@ -28,7 +28,8 @@ const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_
         for (int i = 0; i < n; ++i) {
             const Instance& e = t[i];
             if (e.bm == q.bm && e.bn == q.bn && e.bk == q.bk && e.d == q.pipe_depth && e.waves == q.waves &&
-                e.mfma == mfma && e.half == q.half_stage && e.fp16 == fp16 && e.a_kc == a_kc && e.b_kc == b_kc && e.conv == conv)
+                e.mfma == mfma && e.half == q.half_stage && e.loaders == (q.loader_waves == 0 ? q.waves : q.loader_waves) &&
+                e.fp16 == fp16 && e.a_kc == a_kc && e.b_kc == b_kc && e.conv == conv)
                 return &e;
         }
     }
@@ -36,24 +37,23 @@ const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_
 }
 
 igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
-    (void)conv;
     constexpr int64_t kCUs = 256;
     // Enough 256x256 tiles for every CU: the largest tile (least global and LDS
-    // traffic per flop), 8 waves, a 4-stage ring of 32-deep K tiles, 16x16x32
-    // MFMAs (which sustain a higher clock than 32x32x16 under full load).
+    // traffic per flop), 8 waves.  GEMM: 64-deep K tiles (128-byte rows load
+    // faster) in a 2.5-stage ring, 16x16x32 MFMAs (which hold a higher clock
+    // than 32x32x16 under load), loads issued by one wave per SIMD.  Conv:
+    // 32-deep K tiles in a 4-stage ring with 32x32x16 MFMAs, every wave loading
+    // (measured fastest for its im2col address stream).
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= kCUs) return igc_tune_t{256, 256, 32, 4, 8, 16, 0, 1};
-    // Otherwise 128x128 tiles, and split K until every CU has a workgroup
-    // (each split keeps at least 2048 of K).
+    if (t256 >= kCUs)
+        return conv ? igc_tune_t{256, 256, 32, 4, 8, 32, 0, 8, 1, 0} : igc_tune_t{256, 256, 64, 2, 8, 16, 1, 4, 1, 0};
+    // Otherwise 128x128 tiles; when even those leave CUs idle and K is deep
+    // (at least 2048 per CU's share), stream-K over every CU balances the K
+    // work; shallow K runs one tile per workgroup.
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    int64_t S = 1;
-    if (t128 > 0 && t128 < kCUs) {
-        S = (kCUs + t128 - 1) / t128;
-        if (S > K / 2048) S = K / 2048;
-        if (S > 16) S = 16;
-        if (S < 1) S = 1;
-    }
-    return igc_tune_t{128, 128, 64, 4, 4, 32, 0, (int)S};
+    if (t128 > 0 && t128 < kCUs && K / 2048 >= 2)
+        return igc_tune_t{128, 128, 64, 4, 4, 32, 0, 4, 1, (int)kCUs};
+    return igc_tune_t{128, 128, 64, 4, 4, 32, 0, 4, 1, 0};
 }
 
 }  // namespace igc

@@ -17,9 +17,10 @@
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *   never frees or retains them and keeps no per-call state; calls are
  *   thread-safe.  A call that splits K takes a temporary fp32 workspace
- *   (k_splits * M * N * 4 bytes, N rounded up to 4) with hipMallocAsync on
- *   `stream` and releases it with hipFreeAsync on the same stream; no other
- *   call allocates.
+ *   (k_splits * M * N * 4 bytes, N rounded up to 4), and a stream-K call one
+ *   of G * BM * BN * 4 bytes plus G flags, with hipMallocAsync on `stream`
+ *   and releases it with hipFreeAsync on the same stream; no other call
+ *   allocates.
  * - Each call only validates its arguments and enqueues work on `stream`
  *   (a hipStream_t; NULL = the default stream).  It returns before the GPU
  *   finishes; synchronise the stream to observe the result.
@@ -61,14 +62,24 @@ typedef enum { IGC_OUT_F32 = 0, IGC_OUT_BF16 = 1, IGC_OUT_F16 = 2 } igc_out_t;
  * 8: two per SIMD), the MFMA block edge (32: v_mfma_f32_32x32x16, 16:
  * v_mfma_f32_16x16x32; 0 means 32), half_stage (1: the ring holds one more
  * operand tile, A or B, than PIPE_DEPTH whole stages, i.e. 2*PIPE_DEPTH+1
- * operand slots), and k_splits (<= 1: none; S > 1: split K into up to S
- * ranges computed by separate workgroups whose fp32 partial tiles are summed
- * in split order by a second kernel).  Only compiled (bm, bn, bk, pipe_depth,
- * waves, mfma, half_stage) combinations are accepted (see
- * igc_tune_supported); NULL selects the built-in choice for the shape (which
- * splits K when the output has too few tiles to occupy every CU). */
+ * operand slots), loader_waves (how many of the waves issue the global->LDS
+ * loads; 0 or `waves` = every wave, 4 of 8 = one per SIMD), k_splits (<= 1:
+ * none; S > 1: split K into up to S ranges
+ * computed by separate workgroups whose fp32 partial tiles are summed in
+ * split order by a second kernel), and stream_k (0: none; G > 0: a
+ * persistent grid of G workgroups takes equal runs of the tiles' K ranges, in
+ * units of one ring period; a tile shared by several runs is finished by the
+ * workgroup that computes its last K unit, which adds the fp32 partials of
+ * the others in a fixed order, so results are deterministic).  k_splits > 1
+ * together with stream_k > 0, or stream_k < 0, is IGC_ERR_INVALID_VALUE.  Only
+ * compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves)
+ * combinations are accepted (see igc_tune_supported); NULL selects the built-in choice for the
+ * shape (which splits K when the output has too few tiles to occupy every
+ * CU).  Stream-K assumes the G workgroups are dispatched in index order (a
+ * workgroup only waits on lower-numbered ones); its wait is bounded, so a
+ * violation yields wrong results rather than a hang. */
 typedef struct {
-    int bm, bn, bk, pipe_depth, waves, mfma, half_stage, k_splits;
+    int bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves, k_splits, stream_k;
 } igc_tune_t;
 
 /*
@@ -130,7 +141,7 @@ igc_status_t conv2d_nhwc_implicit_gemm_ex(int N, int H, int W, int C, int K, int
                                           const void *x, const void *w, void *y, igc_out_t y_type, int fp16,
                                           const igc_tune_t *tune, igc_stream_t stream);
 
-/* 1 if (bm, bn, bk, pipe_depth, waves, mfma, half_stage) is a compiled configuration, else 0. */
+/* 1 if (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves) is a compiled configuration, else 0. */
 int igc_tune_supported(const igc_tune_t *tune);
 
 /* The configuration the library picks for an M x N x K problem (conv != 0: the

@@ -59,6 +59,8 @@ FAKE = 1 << 20  # a 16-byte aligned address that is never dereferenced (validati
     (dict(K=60, lda=60), igc.IGC_ERR_MISALIGNED),       # 60 * 2 bytes is not a multiple of 16
     (dict(ldc=66, c_type=igc.OUT_BF16), igc.IGC_ERR_MISALIGNED),
     (dict(tune=(64, 64, 64, 9, 4)), igc.IGC_ERR_UNSUPPORTED),
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 0, 2, 256)), igc.IGC_ERR_INVALID_VALUE),  # split-K and stream-K together
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, -1)), igc.IGC_ERR_INVALID_VALUE),
     (dict(M=0), igc.IGC_OK),                            # empty output: no-op
     (dict(N=0), igc.IGC_OK),
 ])
@@ -133,14 +135,17 @@ def test_probe_dma_validation(args, expect):
 def test_tune_table_fits_lds():
     """Every compiled ring fits the 160 KB of LDS of one CU (a stage costs (BM+BN)*BK*2 bytes)."""
     tunes = igc.tunes()
-    assert (256, 256, 64, 2, 4, 32, 0) in tunes and (256, 256, 32, 5, 8, 32, 0) in tunes
-    assert (256, 256, 32, 4, 8, 16, 0) in tunes and (256, 256, 64, 2, 4, 16, 1) in tunes
-    for (bm, bn, bk, d, w, mi, h) in tunes:
-        lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h))
+    assert (256, 256, 64, 2, 4, 32, 0, 4) in tunes and (256, 256, 32, 5, 8, 32, 0, 8) in tunes
+    assert (256, 256, 32, 4, 8, 16, 0, 8) in tunes and (256, 256, 64, 2, 8, 16, 1, 4) in tunes
+    for (bm, bn, bk, d, w, mi, h, lw) in tunes:
+        assert 1 <= lw <= w and w % lw == 0
+        lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw))
         U = 2 * d + h
         assert lds == ((bm + bn) * bk * 2 * d if U % 2 == 0 else U * max(bm, bn) * bk * 2)
         assert lds <= 160 * 1024
-        assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h)) == 1
+        assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, lw)) == 1
+        if lw == w:  # loader_waves 0 means every wave
+            assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, 0)) == 1
     assert igc.igc_tune_supported((256, 256, 64, 3, 4)) == 0  # 192 KB: over budget, not compiled
     assert igc.igc_tune_supported((256, 256, 64, 2, 6)) == 0
     assert igc.igc_tune_supported((256, 256, 32, 4, 8, 8)) == 0  # no 8x8 MFMA block
@@ -149,17 +154,19 @@ def test_tune_table_fits_lds():
     assert igc.igc_tune_supported((256, 256, 32, 5, 8, 16)) == 0  # 5 stages x 1 k-step: odd fragment parity
 
 
-@pytest.mark.parametrize("shape,expect", [
-    ((8192, 8192, 8192), ((256, 256, 32, 4, 8, 16, 0), 1)),      # enough 256x256 tiles for 256 CUs: no split
-    ((100352, 256, 2304), ((256, 256, 32, 4, 8, 16, 0), 1)),     # the 3x3 conv's GEMM view
-    ((2048, 1024, 16384), ((128, 128, 64, 4, 4, 32, 0), 2)),     # 128 tiles of 128x128: split K in two
-    ((1000, 1000, 65536), ((128, 128, 64, 4, 4, 32, 0), 4)),     # 64 tiles: four splits
-    ((128, 96, 200), ((128, 128, 64, 4, 4, 32, 0), 1)),          # too little K to split
-    ((0, 5, 7), ((128, 128, 64, 4, 4, 32, 0), 1)),
+@pytest.mark.parametrize("shape,conv,expect", [
+    ((8192, 8192, 8192), 0, ((256, 256, 64, 2, 8, 16, 1, 4), 1, 0)),   # 1024 tiles of 256x256: data-parallel
+    ((100352, 256, 2304), 1, ((256, 256, 32, 4, 8, 32, 0, 8), 1, 0)),  # the 3x3 conv's GEMM view
+    ((100352, 256, 2304), 0, ((256, 256, 64, 2, 8, 16, 1, 4), 1, 0)),  # the same shape as a GEMM
+    ((2048, 1024, 16384), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 128 tiles of 128x128: stream-K
+    ((1000, 1000, 65536), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 64 tiles
+    ((1000, 1000, 3000), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),    # too little K to share
+    ((128, 96, 200), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),
+    ((0, 5, 7), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),
 ])
-def test_default_tune(shape, expect):
-    t = igc.igc_default_tune(*shape)
-    assert (t.astuple(), t.k_splits) == expect
+def test_default_tune(shape, conv, expect):
+    t = igc.igc_default_tune(*shape, conv=conv)
+    assert (t.astuple(), t.k_splits, t.stream_k) == expect
     assert igc.igc_tune_supported(t) == 1
 
 

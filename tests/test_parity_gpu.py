@@ -198,9 +198,10 @@ def test_k_chain_tags(tune):
         assert np.all(y == float(tags.sum())), f"k-chain tune={tune} K={K}: {np.unique(y)[:5]}"
 
 
-@pytest.mark.parametrize("tune", [(128, 128, 64, 4, 4, 32, 0), (256, 256, 32, 4, 8, 32, 0), (256, 128, 64, 3, 4, 32, 0),
-                                  (256, 256, 32, 4, 8, 16, 0), (128, 128, 64, 4, 4, 16, 0),
-                                  (256, 256, 64, 2, 4, 16, 1)])
+@pytest.mark.parametrize("tune", [(128, 128, 64, 4, 4, 32, 0, 0), (256, 256, 32, 4, 8, 32, 0, 0),
+                                  (256, 128, 64, 3, 4, 32, 0, 0), (256, 256, 32, 4, 8, 16, 0, 0),
+                                  (128, 128, 64, 4, 4, 16, 0, 0), (256, 256, 64, 2, 8, 16, 1, 4),
+                                  (256, 256, 32, 4, 8, 16, 0, 4)])
 def test_split_k(tune):
     """K split over 2..8 workgroups per tile, fp32 partials summed in split order: ragged K, every layout."""
     cases = [(300, 270, 1000, "row", "row", 2, "f32", "bf16"), (257, 129, 777, "row", "col", 3, "bf16", "bf16"),
@@ -216,7 +217,7 @@ def test_split_k_deterministic_and_exact():
     oracle bit for bit and repeats bit for bit."""
     M, N, K = 384, 256, 3000
     A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", 3000, 256, "bf16", ("int", 4), ("int", 4), seed=8)
-    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=(128, 128, 64, 4, 4, 32, 0, 6))[0]
+    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=(128, 128, 64, 4, 4, 32, 0, 0, 6))[0]
             for _ in range(2)]
     ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row")
     assert np.array_equal(outs[0], ref) and np.array_equal(outs[0], outs[1])
@@ -227,9 +228,71 @@ def test_conv_split_k():
     x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=41)
     for S in (2, 3):
         say(f"conv split-K S={S}")
-        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=(128, 128, 64, 4, 4, 32, 0, S))
+        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=(128, 128, 64, 4, 4, 32, 0, 0, S))
         ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
         assert_close(y, ref, Sabs, "bf16", f"conv split {S}")
+
+
+SK_TUNES = [(256, 256, 32, 4, 8, 16, 0, 0), (128, 128, 64, 4, 4, 32, 0, 0), (256, 256, 64, 2, 4, 32, 1, 0),
+            (256, 256, 32, 5, 8, 32, 0, 0), (256, 256, 64, 1, 4, 32, 0, 0), (256, 256, 64, 2, 8, 16, 1, 4),
+            (256, 256, 32, 4, 8, 16, 0, 4)]
+
+
+@pytest.mark.parametrize("tune", SK_TUNES)
+def test_stream_k(tune):
+    """Stream-K over G persistent workgroups: runs that start and end inside tiles, runs inside one tile, more
+    workgroups than K units (G clamps), ragged K, every layout and dtype."""
+    cases = [(300, 270, 1000, "row", "row", 7, "f32", "bf16"), (257, 129, 777, "row", "col", 13, "bf16", "bf16"),
+             (520, 390, 4096, "col", "row", 64, "f16", "fp16"), (64, 72, 200, "col", "col", 300, "f32", "bf16"),
+             (1000, 1000, 6144, "row", "row", 256, "f32", "fp16"), (513, 777, 2304, "row", "row", 33, "f32", "bf16")]
+    for (M, N, K, la, lb, G, out, dtype) in cases:
+        say(f"stream-K tune {tune} G={G} {M}x{N}x{K} {la}/{lb} {dtype}->{out}")
+        gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=400 + G, tune=tuple(tune) + (1, G))
+
+
+def test_stream_k_deterministic_and_exact():
+    """Integer inputs: partials and the owner's fixed-order sum are exact, so stream-K equals the oracle bit for
+    bit, and repeats bit for bit; the K-chain tags catch a dropped, repeated or misplaced K run."""
+    M, N, K = 700, 520, 3000
+    A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", 3000, 520, "bf16", ("int", 4), ("int", 4), seed=9)
+    ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row")
+    for G in (5, 37, 256):
+        outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32",
+                         tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, G))[0] for _ in range(2)]
+        assert np.array_equal(outs[0], ref) and np.array_equal(outs[0], outs[1]), f"G={G}"
+    M, N, K = 520, 136, 2400
+    A = np.full((M, K), 0x3F80, np.uint16)
+    tags = np.array([(k // 32) % 7 + 1 for k in range(K)], np.float32)
+    Bt = torch.from_numpy(np.repeat(tags[:, None], N, axis=1)).to(torch.bfloat16).view(torch.int16).numpy()
+    for G in (3, 11, 100):
+        y, _ = run_gemm(M, N, K, A, K, "row", Bt.view(np.uint16), N, "row", out="f32",
+                        tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, G))
+        assert np.all(y == float(tags.sum())), f"k-chain stream-K G={G}: {np.unique(y)[:5]}"
+
+
+def test_stream_k_rejects_mixed_with_split():
+    A = torch.zeros(64 * 64, dtype=torch.int16, device="cuda")
+    C = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
+    st = igc.gemm_bf16_ex(64, 64, 64, A, 64, igc.ROW_MAJOR, A, 64, igc.ROW_MAJOR, C, 64, igc.OUT_F32,
+                          (256, 256, 32, 4, 8, 16, 0, 0, 2, 8))
+    assert st == igc.IGC_ERR_INVALID_VALUE
+
+
+def test_conv_stream_k():
+    N, H, W, C, K = 2, 9, 7, 256, 136
+    x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=43)
+    ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
+    for tune in ((256, 256, 32, 4, 8, 16, 0, 0, 1, 5), (256, 256, 32, 4, 8, 32, 0, 0, 1, 3),
+                 (128, 128, 64, 4, 4, 32, 0, 0, 1, 7), (256, 256, 64, 2, 8, 16, 1, 4, 1, 9)):
+        say(f"conv stream-K {tune}")
+        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=tune)
+        assert_close(y, ref, Sabs, "bf16", f"conv stream-K {tune}")
+    # channels not a multiple of the K tile: per-lane tap split inside each run
+    N, H, W, C, K = 1, 8, 6, 24, 40
+    x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=44)
+    ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
+    y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="f32", tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, 2))
+    assert_close(y, ref, Sabs, "f32", "conv stream-K C=24")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
