@@ -111,6 +111,70 @@ def cpu_baseline(gcfg, ccfg, A, B, x, w):
                       f"({step_s:.0f} s)"}
 
 
+def workload_cost(c):
+    """(flops, algorithmic HBM bytes: inputs read once, output written once) of a named workload."""
+    out_bytes = 4 if c["out"] == "f32" else 2
+    if c["kind"] == "gemm":
+        return gemm_flops(c), 2 * (c["M"] * c["K"] + c["K"] * c["N"]) + out_bytes * c["M"] * c["N"]
+    P, Q = conv_geometry(c)
+    return conv_flops(c), (2 * (c["N"] * c["H"] * c["W"] * c["C"] + c["K"] * c["R"] * c["S"] * c["C"]) +
+                           out_bytes * c["N"] * P * Q * c["K"])
+
+
+def run_suite(reps, warmup):
+    """Every named workload with the library's built-in tile: mean and median launch time (HIP events on the
+    launch stream), TFLOP/s, and algorithmic HBM bandwidth."""
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name, c in inputs.WORKLOADS.items():
+        out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[c["out"]]
+        if c["kind"] == "gemm":
+            A, lda, B, ldb = inputs.workload_operands(name)
+            dA = torch.from_numpy(A.view(np.int16)).cuda()
+            dB = torch.from_numpy(B.view(np.int16)).cuda()
+            dC = torch.empty((c["M"], c["N"]), dtype=out_dt, device="cuda")
+            fn = igc.gemm_fp16 if c["dtype"] == "fp16" else igc.gemm_bf16
+            la, lb = (igc.ROW_MAJOR if c[k] == "row" else igc.COL_MAJOR for k in ("la", "lb"))
+            call = lambda: igc.check(fn(c["M"], c["N"], c["K"], dA, lda, la, dB, ldb, lb, dC, c["N"],
+                                        igc.OUT_CODES[c["out"]], stream))
+            t = igc.igc_default_tune(c["M"], c["N"], c["K"])
+        else:
+            x, w = inputs.workload_operands(name)
+            P, Q = conv_geometry(c)
+            dx = torch.from_numpy(x.view(np.int16)).cuda()
+            dw = torch.from_numpy(w.view(np.int16)).cuda()
+            dy = torch.empty((c["N"] * P * Q * c["K"],), dtype=out_dt, device="cuda")
+            call = lambda: igc.check(igc.conv2d_nhwc_implicit_gemm_ex(
+                c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"], c["ph"], c["pw"], c["dh"],
+                c["dw"], dx, dw, dy, igc.OUT_CODES[c["out"]], 1 if c["dtype"] == "fp16" else 0, None, stream))
+            t = igc.igc_default_tune(c["N"] * P * Q, c["K"], c["R"] * c["S"] * c["C"], conv=1)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            call()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+        flops, nbytes = workload_cost(c)
+        tune = ",".join(map(str, t.astuple())) + (f" k_splits={t.k_splits}" if t.k_splits > 1 else "") + \
+            (f" stream_k={t.stream_k}" if t.stream_k > 0 else "")
+        row = {"workload": name, "us_mean": round(float(ms.mean()) * 1e3, 1),
+               "us_median": round(float(np.median(ms)) * 1e3, 1),
+               "tflops": round(flops / (ms.mean() * 1e-3) / 1e12, 1),
+               "hbm_gbs_algorithmic": round(nbytes / (ms.mean() * 1e-3) / 1e9, 1), "tile": tune}
+        log(f"{name:40s} {row['us_mean']:9.1f} us  {row['tflops']:7.1f} TFLOP/s  {row['hbm_gbs_algorithmic']:8.1f} GB/s"
+            f"  tile {tune}")
+        rows.append(row)
+        del call
+        torch.cuda.empty_cache()
+    print(json.dumps({"suite": rows, "steps": reps, "warmup": warmup,
+                      "note": "inputs resident in HBM; HIP events on the launch stream around each launch"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +183,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", type=str, default=None, help="bm,bn,bk,depth,waves,mfma,half_stage[,k_splits] for the GEMM (default: built-in)")
     ap.add_argument("--conv-tune", type=str, default=None, help="bm,bn,bk,depth,waves,mfma,half_stage[,k_splits] for the conv (default: built-in)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the step: time every named workload in implicit_gemm_conv_amd/inputs.py with the "
+                         "built-in tile and print one JSON line with all of them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run one plain device copy of MIB MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -132,6 +199,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     igc.lib()  # the HIP library must be built: no fallback
+    if args.suite:
+        run_suite(max(args.steps, 5), max(args.warmup, 1))
+        return
     gtune = tuple(int(v) for v in args.tune.split(",")) if args.tune else None
     ctune = tuple(int(v) for v in args.conv_tune.split(",")) if args.conv_tune else None
 

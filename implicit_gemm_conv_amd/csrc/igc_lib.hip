@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "igc.h"
 #include "instances.hpp"
 #include "mainloop.hpp"
@@ -22,6 +24,22 @@
 namespace igc {
 
 static bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Stream-K flags are raised to a per-call epoch, written with its complement,
+// so a workspace holding flags of earlier calls (or any other data) needs no
+// clearing: only the pair (epoch, ~epoch) of this call counts as raised.  The
+// epoch is a call counter passed through a bijective 32-bit mix (so
+// consecutive calls differ in many bits), keeping 31 bits.
+static std::atomic<uint32_t> g_stream_k_calls{0};
+static int next_stream_k_epoch() {
+    uint32_t x = g_stream_k_calls.fetch_add(1, std::memory_order_relaxed) + 0x9e3779b9u;
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return (int)(x & 0x7fffffffu);
+}
 
 static int out_size(igc_out_t t) { return t == IGC_OUT_F32 ? 4 : 2; }
 
@@ -61,18 +79,17 @@ static igc_status_t launch(const Plan& pl, Params p, hipStream_t stream) {
         const size_t part_bytes = (size_t)G * inst->bm * inst->bn * sizeof(float);
         char* ws = nullptr;
         (void)hipGetLastError();
-        if (hipMallocAsync((void**)&ws, part_bytes + (size_t)G * sizeof(int), stream) != hipSuccess)
+        if (hipMallocAsync((void**)&ws, part_bytes + (size_t)G * 2 * sizeof(int), stream) != hipSuccess)
             return IGC_ERR_HIP;
         p.sk_grid = (int)G;
         p.sk_units = UT;
         p.sk_ws = (float*)ws;
         p.sk_flags = (int*)(ws + part_bytes);
+        p.sk_epoch = next_stream_k_epoch();
         p.k_splits = 1;
-        hipError_t e = hipMemsetAsync(p.sk_flags, 0, (size_t)G * sizeof(int), stream);
         Params arg = p;
         void* args[] = {&arg};
-        if (e == hipSuccess)
-            e = hipLaunchKernel(inst->fn, dim3((unsigned)G), dim3(64 * inst->waves), args, 0, stream);
+        hipError_t e = hipLaunchKernel(inst->fn, dim3((unsigned)G), dim3(64 * inst->waves), args, 0, stream);
         (void)hipFreeAsync(ws, stream);
         if (e != hipSuccess) return IGC_ERR_HIP;
         return hipGetLastError() == hipSuccess ? IGC_OK : IGC_ERR_HIP;

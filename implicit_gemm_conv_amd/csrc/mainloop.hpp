@@ -102,13 +102,16 @@ struct Params {
     // stream-K (sk_grid > 0 workgroups): the tiles' K ranges, in units of the
     // ring period (sk_units per tile), are cut into sk_grid equal runs; a
     // workgroup whose run ends inside a tile publishes an fp32 partial tile in
-    // sk_ws (one BM x BN slot per workgroup) and raises sk_flags[its index];
+    // sk_ws (one BM x BN slot per workgroup) and raises its flag, the pair
+    // sk_flags[2*index .. 2*index+1] = (epoch, ~epoch);
     // the workgroup that computes the tile's last K unit adds the partials of
-    // the lower workgroups in descending order and stores the tile.
+    // the lower workgroups in descending order and stores the tile.  Flags
+    // are raised to this call's epoch, so the workspace needs no clearing.
     int sk_grid;
     int64_t sk_units;
     float* sk_ws;
     int* sk_flags;
+    int sk_epoch;  // value a flag takes when raised in this call (31 bits, distinct from earlier calls)
     int conv_uniform;  // Cin % BK == 0: every K tile lies within one filter tap
     int tpt;           // K tiles per filter tap (Cin / BK) when conv_uniform
     uint32_t cin_magic, s_magic, tpt_magic;  // fastdiv multipliers for Cin, S and tpt
@@ -639,7 +642,7 @@ struct Mainloop {
 
     // Writes the partial tile, waits until this wave's stores are complete,
     // and (once every wave is there) raises the flag.
-    __device__ __forceinline__ void sk_publish(const Acc (&acc)[FM][FN], float* part, int* flag) {
+    __device__ __forceinline__ void sk_publish(const Acc (&acc)[FM][FN], float* part, int* flag, int epoch) {
         typedef __attribute__((ext_vector_type(4))) int i32x4_t;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(part);
 #pragma unroll
@@ -654,18 +657,22 @@ struct Mainloop {
                 }
         wait_vmcnt<0>();
         __syncthreads();
-        if (threadIdx.x == 0)
-            __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(flag), 0, 0, kCoherent);
+        if (threadIdx.x == 0) {
+            typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2_t{epoch, ~epoch}, make_rsrc(flag), 0, 0, kCoherent);
+        }
     }
 
     // Waits for a lower workgroup's flag (bounded: every wave leaves the loop
     // even if the flag never rises) and adds its partial tile.
-    __device__ __forceinline__ void sk_collect(Acc (&acc)[FM][FN], const float* part, int* flag) {
+    __device__ __forceinline__ void sk_collect(Acc (&acc)[FM][FN], const float* part, int* flag, int epoch) {
         typedef __attribute__((ext_vector_type(4))) int i32x4_t;
         if (threadIdx.x == 0) {
             const __amdgpu_buffer_rsrc_t rf = make_rsrc(flag);
+            typedef __attribute__((ext_vector_type(2))) int i32x2_t;
             for (int spins = 0; spins < (1 << 24); ++spins) {
-                if (__builtin_amdgcn_raw_buffer_load_b32(rf, 0, 0, kCoherentVolatile) != 0) break;
+                const i32x2_t f = __builtin_amdgcn_raw_buffer_load_b64(rf, 0, 0, kCoherentVolatile);
+                if (f[0] == epoch && f[1] == ~epoch) break;
                 __builtin_amdgcn_s_sleep(2);
             }
         }
@@ -1013,12 +1020,13 @@ __device__ __forceinline__ void stream_k(const Params p) {
         with_variant<C>(p, [&](auto v) __attribute__((always_inline)) {
             run_tile<C, decltype(v)::value>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
                 if (u1 < UT) {
-                    ml.sk_publish(acc, p.sk_ws + (int64_t)g * (C::BM * C::BN), p.sk_flags + g);
+                    ml.sk_publish(acc, p.sk_ws + (int64_t)g * (C::BM * C::BN), p.sk_flags + 2 * g, p.sk_epoch);
                 } else {
                     // owner: add the partials of the lower workgroups sharing this tile
                     const int64_t tile_start = tau * UT;
                     for (int gp = g - 1; gp >= 0 && sk_end(total, G, gp) > tile_start; --gp)
-                        ml.sk_collect(acc, p.sk_ws + (int64_t)gp * (C::BM * C::BN), p.sk_flags + gp);
+                        ml.sk_collect(acc, p.sk_ws + (int64_t)gp * (C::BM * C::BN), p.sk_flags + 2 * gp,
+                                      p.sk_epoch);
                     ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
                 }
             });

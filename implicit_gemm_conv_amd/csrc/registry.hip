@@ -45,12 +45,15 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
     // 32-deep K tiles in a 4-stage ring with 32x32x16 MFMAs, every wave loading
     // (measured fastest for its im2col address stream).
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= kCUs)
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    // 256x256 tiles unless they pad the output by more than a third more than
+    // 128x128 tiles do (a 64-wide N, say) while 128x128 still fills the CUs
+    const bool wasteful = t256 * 65536 * 3 > t128 * 16384 * 4 && t128 >= kCUs;
+    if (t256 >= kCUs && !wasteful)
         return conv ? igc_tune_t{256, 256, 32, 4, 8, 32, 0, 8, 1, 0} : igc_tune_t{256, 256, 64, 2, 8, 16, 1, 4, 1, 0};
     // Otherwise 128x128 tiles; when even those leave CUs idle and K is deep
     // (at least 2048 per CU's share), stream-K over every CU balances the K
     // work; shallow K runs one tile per workgroup.
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (t128 > 0 && t128 < kCUs && K / 2048 >= 2)
         return igc_tune_t{128, 128, 64, 4, 4, 32, 0, 4, 1, (int)kCUs};
     return igc_tune_t{128, 128, 64, 4, 4, 32, 0, 4, 1, 0};

@@ -9,8 +9,8 @@ one flat vector of its whole storage including any leading-dimension padding),
 then each value is rounded to nearest-even to bf16 or fp16 once.  The GPU and
 the oracle consume the same stored bits.
 
-The named workloads below are the five shapes this library is measured and
-tested on; sizes and distributions are synthetic stand-ins for the pages'
+The named workloads below are the shapes this library is measured and tested
+on; sizes and distributions are synthetic stand-ins for the pages'
 GEMM/convolution workloads (the pages publish no dataset).
 """
 import numpy as np
@@ -35,6 +35,20 @@ WORKLOADS = {
     # deep K, ragged M/N edges, fp16
     "gemm_fp16_1000x1000x65536": dict(kind="gemm", M=1000, N=1000, K=65536, la=ROW, lb=ROW, dtype="fp16", out="f32",
                                       a_dist=("uniform", 0.5), b_dist=("uniform", 0.5), seed=5),
+    # more convolution iterators on the same mainloop: stride 2, a 1x1 filter,
+    # channels not a multiple of 64, odd image sizes
+    "conv_bf16_n32_56x56_c256_k512_3x3_s2": dict(kind="conv", N=32, H=56, W=56, C=256, K=512, R=3, S=3, sh=2, sw=2,
+                                                 ph=1, pw=1, dh=1, dw=1, dtype="bf16", out="bf16",
+                                                 a_dist=("normal", 1.0), b_dist=("normal", 0.02), seed=6),
+    "conv_bf16_n32_56x56_c256_k64_1x1": dict(kind="conv", N=32, H=56, W=56, C=256, K=64, R=1, S=1, sh=1, sw=1,
+                                             ph=0, pw=0, dh=1, dw=1, dtype="bf16", out="bf16",
+                                             a_dist=("normal", 1.0), b_dist=("normal", 0.06), seed=7),
+    "conv_bf16_n32_28x28_c96_k192_3x3": dict(kind="conv", N=32, H=28, W=28, C=96, K=192, R=3, S=3, sh=1, sw=1,
+                                             ph=1, pw=1, dh=1, dw=1, dtype="bf16", out="bf16",
+                                             a_dist=("normal", 1.0), b_dist=("normal", 0.03), seed=8),
+    "conv_bf16_n16_27x27_c256_k256_3x3": dict(kind="conv", N=16, H=27, W=27, C=256, K=256, R=3, S=3, sh=1, sw=1,
+                                              ph=1, pw=1, dh=1, dw=1, dtype="bf16", out="bf16",
+                                              a_dist=("normal", 1.0), b_dist=("normal", 0.02), seed=9),
 }
 
 _TORCH = {"bf16": torch.bfloat16, "fp16": torch.float16}

@@ -15,10 +15,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *   never frees or retains them and keeps no per-call state; calls are
+ *   never frees or retains them and keeps no per-call state (beyond a
+ *   process-wide call counter that tags stream-K flags); calls are
  *   thread-safe.  A call that splits K takes a temporary fp32 workspace
  *   (k_splits * M * N * 4 bytes, N rounded up to 4), and a stream-K call one
- *   of G * BM * BN * 4 bytes plus G flags, with hipMallocAsync on `stream`
+ *   of G * BM * BN * 4 bytes plus 8 bytes per workgroup, with hipMallocAsync on `stream`
  *   and releases it with hipFreeAsync on the same stream; no other call
  *   allocates.
  * - Each call only validates its arguments and enqueues work on `stream`
@@ -70,7 +71,10 @@ typedef enum { IGC_OUT_F32 = 0, IGC_OUT_BF16 = 1, IGC_OUT_F16 = 2 } igc_out_t;
  * persistent grid of G workgroups takes equal runs of the tiles' K ranges, in
  * units of one ring period; a tile shared by several runs is finished by the
  * workgroup that computes its last K unit, which adds the fp32 partials of
- * the others in a fixed order, so results are deterministic).  k_splits > 1
+ * the others in a fixed order, so results are deterministic; each flag is
+ * raised as the pair (epoch, ~epoch) with a per-call 31-bit epoch, so the
+ * workspace is never cleared, and only reused memory that happens to hold
+ * exactly that pair where a flag lies could be mistaken for a raised flag).  k_splits > 1
  * together with stream_k > 0, or stream_k < 0, is IGC_ERR_INVALID_VALUE.  Only
  * compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves)
  * combinations are accepted (see igc_tune_supported); NULL selects the built-in choice for the

@@ -161,6 +161,7 @@ def test_tune_table_fits_lds():
     ((2048, 1024, 16384), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 128 tiles of 128x128: stream-K
     ((1000, 1000, 65536), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 64 tiles
     ((1000, 1000, 3000), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),    # too little K to share
+    ((100352, 64, 256), 1, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),    # 1x1 conv with 64 outputs: 128-wide tiles
     ((128, 96, 200), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),
     ((0, 5, 7), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),
 ])

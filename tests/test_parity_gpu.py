@@ -113,16 +113,19 @@ def test_workload_large_gemm_sampled(name, out):
     say(f"  {rows.size} sampled outputs, max err/bound {r:.3g}")
 
 
-@pytest.mark.parametrize("out", [None, "f32"])
-def test_workload_conv_sampled(out):
-    name = "conv_bf16_n32_56x56_c256_k256_3x3"
+CONV_WORKLOADS = [n for n, c in inputs.WORKLOADS.items() if c["kind"] == "conv"]
+
+
+@pytest.mark.parametrize("name,out", [(n, None) for n in CONV_WORKLOADS] +
+                         [("conv_bf16_n32_56x56_c256_k256_3x3", "f32")])
+def test_workload_conv_sampled(name, out):
     cfg = inputs.WORKLOADS[name]
     out = out or cfg["out"]
     say(f"workload {name} -> {out}")
     x, w = inputs.workload_operands(name)
     geo = dict(sh=cfg["sh"], sw=cfg["sw"], ph=cfg["ph"], pw=cfg["pw"], dh=cfg["dh"], dw=cfg["dw"])
     y, _ = run_conv(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], x, w, out=out, **geo)
-    rng = np.random.default_rng(4)
+    rng = np.random.default_rng(cfg["seed"])
     idx = list(rng.integers(0, y.size, 12000))
     P, Q, K = y.shape[1], y.shape[2], y.shape[3]
     # every output channel of the four image corners of the first and last image (padding taps)
