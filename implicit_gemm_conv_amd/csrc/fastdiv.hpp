@@ -23,7 +23,9 @@ IGC_FD_HD inline uint32_t fastdiv_magic(uint32_t d) {
 // one (the rounding error of m adds less than n / 2^32 < 1), so one compare
 // fixes it.
 IGC_FD_HD inline uint32_t fastdiv(uint32_t n, uint32_t d, uint32_t m) {
-    const uint32_t q = m ? (uint32_t)(((uint64_t)n * m) >> 32) : n;
+    // both arms computed, then selected: no branch inside a caller's loop
+    const uint32_t hi = (uint32_t)(((uint64_t)n * m) >> 32);
+    const uint32_t q = m ? hi : n;
     return q * d > n ? q - 1 : q;
 }
 

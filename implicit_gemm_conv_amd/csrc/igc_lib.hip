@@ -228,6 +228,7 @@ static igc_status_t conv_any(bool fp16, int N, int H, int W, int C, int K, int R
     p.dh = dh;
     p.dw = dw;
     p.conv_uniform = (C % inst->bk) == 0;
+    p.conv_masks = R <= 16 && S <= 16;
     p.tpt = p.conv_uniform ? C / inst->bk : 1;
     p.cin_magic = fastdiv_magic((uint32_t)C);
     p.s_magic = fastdiv_magic((uint32_t)S);

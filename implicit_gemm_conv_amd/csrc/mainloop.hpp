@@ -113,6 +113,7 @@ struct Params {
     int* sk_flags;
     int sk_epoch;  // value a flag takes when raised in this call (31 bits, distinct from earlier calls)
     int conv_uniform;  // Cin % BK == 0: every K tile lies within one filter tap
+    int conv_masks;    // R <= 16 and S <= 16: tap validity from per-row bit masks
     int tpt;           // K tiles per filter tap (Cin / BK) when conv_uniform
     uint32_t cin_magic, s_magic, tpt_magic;  // fastdiv multipliers for Cin, S and tpt
 };
@@ -120,8 +121,10 @@ struct Params {
 // Loop variants, chosen per call and compiled as separate loops so that none
 // carries a branch between its MFMAs: GEMM with K % 8 == 0 or convolution
 // whose channel tiles straddle filter taps (PLAIN), K % 8 != 0 (RAGGED),
-// convolution with whole filter taps per K tile (UNIFORM_TAP).
-enum LoopVariant : int { PLAIN = 0, UNIFORM_TAP = 1, RAGGED = 2 };
+// convolution with whole filter taps per K tile (UNIFORM_TAP), and convolution
+// with a filter wider or taller than 16 taps (CONV_GENERIC; the others keep a
+// per-row bit mask of the filter rows and columns that fall inside the image).
+enum LoopVariant : int { PLAIN = 0, UNIFORM_TAP = 1, RAGGED = 2, CONV_GENERIC = 3 };
 
 // XOR swizzle of the 16-byte chunk index within a K-contiguous LDS row of CPR
 // chunks.  On gfx950 the LDS serves a 128-bit read 16 lanes at a time over its
@@ -288,6 +291,7 @@ struct DmaState {
 template <class C, int V, bool LOADER = true>
 struct Mainloop {
     static constexpr bool kRagged = V == RAGGED, kUniformTap = V == UNIFORM_TAP;
+    static constexpr bool kConvMasks = C::CONV && V != CONV_GENERIC;
     // LOADER: this wave issues global->LDS loads (waves 0 .. NL-1)
     using TA = typename C::TA;
     using TB = typename C::TB;
@@ -305,9 +309,15 @@ struct Mainloop {
     DmaState<TA::IPW> da;
     DmaState<TB::IPW> db;
     // im2col: per A instruction, the pixel base offset and top-left input coordinate
-    int conv_pix[C::CONV ? TA::IPW : 1];
-    int conv_h0[C::CONV ? TA::IPW : 1];
-    int conv_w0[C::CONV ? TA::IPW : 1];
+    // masked form: byte offset of the row's pixel at filter tap (0, 0) (may be
+    // negative at the padding) and its tap mask (bit r: filter row r lands in
+    // the image; bit 16+s: filter column s does; 0 for rows past M)
+    int conv_base[kConvMasks ? TA::IPW : 1];
+    uint32_t conv_mask[kConvMasks ? TA::IPW : 1];
+    // generic form: image base, top-left input row and column of the window
+    int conv_pix[C::CONV && !kConvMasks ? TA::IPW : 1];
+    int conv_h0[C::CONV && !kConvMasks ? TA::IPW : 1];
+    int conv_w0[C::CONV && !kConvMasks ? TA::IPW : 1];
     // the swizzled K chunk this lane fetches (same for all its loads of an operand)
     int ca_lane = 0, cb_lane = 0;
     // fragment read offsets (bytes within a stage's operand region)
@@ -344,9 +354,20 @@ struct Mainloop {
                 const int mm = (int)(m < p.M ? m : 0);
                 const int n = mm / PQ, pq = mm - n * PQ;
                 const int pp = pq / p.Q, qq = pq - pp * p.Q;
-                conv_pix[j] = n * p.H * p.W * p.Cin;
-                conv_h0[j] = m < p.M ? pp * p.sh - p.ph : -(1 << 28);  // invalid rows never hit the image
-                conv_w0[j] = qq * p.sw - p.pw;
+                const int h0 = pp * p.sh - p.ph, w0 = qq * p.sw - p.pw;
+                if constexpr (kConvMasks) {
+                    uint32_t mask = 0;
+                    for (int r = 0; r < p.R; ++r)
+                        if ((unsigned)(h0 + r * p.dh) < (unsigned)p.H) mask |= 1u << r;
+                    for (int s = 0; s < p.S; ++s)
+                        if ((unsigned)(w0 + s * p.dw) < (unsigned)p.W) mask |= 1u << (16 + s);
+                    conv_mask[j] = m < p.M ? mask : 0u;
+                    conv_base[j] = (((n * p.H + h0) * p.W + w0) * p.Cin) * 2;
+                } else {
+                    conv_pix[j] = n * p.H * p.W * p.Cin;
+                    conv_h0[j] = m < p.M ? h0 : -(1 << 28);  // invalid rows never hit the image
+                    conv_w0[j] = w0;
+                }
                 da.voff[j] = 0;
             } else if constexpr (C::A_KC) {
                 // A row-major: tile row = m, chunk c covers k = 8c .. 8c+7 of the current K tile
@@ -458,16 +479,28 @@ struct Mainloop {
                     cin = (int)(kg - tap * (uint32_t)p.Cin);
                 }
                 const bool kok = 8 * ca_lane < krem;
-                const int dhr = r * p.dh, dws = s * p.dw;
-                static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
-                    constexpr int j = J;
-                    const int q = j * C::NL + wave;
-                    const int h = conv_h0[j] + dhr;
-                    const int w = conv_w0[j] + dws;
-                    const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
-                    const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
-                    dma16(rs, sa + q * 1024, ok ? off : kOob);
-                });
+                if constexpr (kConvMasks) {
+                    // tap (r, s) of a row is in the image iff both its mask bits are set
+                    const uint32_t need = (1u << (r & 15)) | (1u << (16 + (s & 15)));
+                    const int toff = ((r * p.dh * p.W + s * p.dw) * p.Cin + cin) * 2;
+                    static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = J;
+                        const int q = j * C::NL + wave;
+                        const bool ok = kok && (conv_mask[j] & need) == need;
+                        dma16(rs, sa + q * 1024, ok ? (uint32_t)(conv_base[j] + toff) : kOob);
+                    });
+                } else {
+                    const int dhr = r * p.dh, dws = s * p.dw;
+                    static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = J;
+                        const int q = j * C::NL + wave;
+                        const int h = conv_h0[j] + dhr;
+                        const int w = conv_w0[j] + dws;
+                        const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+                        const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
+                        dma16(rs, sa + q * 1024, ok ? off : kOob);
+                    });
+                }
             } else if constexpr (C::A_KC) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (m0 * p.lda + k0) * 2);
                 const bool kout = 8 * ca_lane >= krem;
@@ -970,7 +1003,9 @@ template <class C, class F>
 __device__ __forceinline__ void with_variant(const Params p, F&& f) {
     if constexpr (C::CONV) {
         // channels are a multiple of 8, so K never is ragged
-        if (p.conv_uniform)
+        if (!p.conv_masks)
+            f(std::integral_constant<int, CONV_GENERIC>{});
+        else if (p.conv_uniform)
             f(std::integral_constant<int, UNIFORM_TAP>{});
         else
             f(std::integral_constant<int, PLAIN>{});

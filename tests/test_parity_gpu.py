@@ -363,6 +363,8 @@ CONV_CASES = [
     (2, 5, 5, 8, 3, 3, 3, 1, 1, 0, 0, 1, 1),      # no padding
     (1, 9, 7, 8, 6, 3, 2, 1, 2, 2, 1, 2, 1),      # dilation, asymmetric filter and stride
     (1, 7, 9, 8, 4, 2, 3, 1, 1, 1, 2, 1, 2),
+    (1, 5, 20, 8, 4, 1, 17, 1, 1, 0, 8, 1, 1),    # 17-tap filter row: the generic (unmasked) address path
+    (2, 20, 6, 16, 8, 17, 2, 1, 1, 8, 0, 1, 1),   # 17 filter rows
     (3, 1, 2, 24, 7, 3, 3, 1, 1, 1, 1, 1, 1),     # tiny image
     (2, 3, 3, 64, 130, 3, 3, 1, 1, 1, 1, 1, 1),   # K not a multiple of 8
     (2, 6, 5, 16, 9, 1, 1, 1, 1, 0, 0, 1, 1),     # 1x1
