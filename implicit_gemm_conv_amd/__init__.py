@@ -47,6 +47,13 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m implicit_gemm_conv_amd.build`")
+        # torch ships its own copy of the HIP runtime; load it first so that the
+        # library binds to the same runtime that allocated the tensors passed in
+        # (with two runtimes in one process, launches on torch's memory fail).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         gemm = [i64, i64, i64, p, i64, i32, p, i64, i32, p, i64, i32]

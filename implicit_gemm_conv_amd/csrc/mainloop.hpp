@@ -844,6 +844,87 @@ __device__ __forceinline__ IGC_LDS char* slot_a() { return slot<C, Ring::slot_of
 template <class C, int u>
 __device__ __forceinline__ IGC_LDS char* slot_b() { return slot<C, Ring::slot_of(C::U, 2 * u + 1)>(); }
 
+// Whole R-byte pieces the ring's slots hold when each piece lies inside one slot.
+template <class C, int R, int S = 0>
+constexpr int stage_pieces() {
+    if constexpr (S >= C::U)
+        return 0;
+    else
+        return C::template slot_bytes<S>() / R + stage_pieces<C, R, S + 1>();
+}
+// Piece w of that packing (slots in order).
+template <class C, int R, int S = 0>
+__device__ __forceinline__ IGC_LDS char* stage_piece(int w) {
+    if constexpr (S >= C::U) {
+        return nullptr;
+    } else {
+        constexpr int n = C::template slot_bytes<S>() / R;
+        if (w < n) return slot<C, S>() + w * R;
+        return stage_piece<C, R, S + 1>(w - n);
+    }
+}
+
+// Output epilogue.  A full tile with a 2-byte output type goes through LDS:
+// after the ring's last reads, each wave writes its WTM x WTN sub-tile,
+// converted, into a private piece of the ring (16-byte chunks of a row
+// XOR-swizzled by the row, so the 2-byte-column writes of an MFMA block spread
+// over the banks), reads it back 16 bytes per lane and stores whole row
+// segments: every store instruction writes WTN*2-byte runs of consecutive
+// addresses instead of 8-byte pieces of 16 or 32 rows, which the memory system
+// retires far faster.  Other tiles and fp32 output store straight from the
+// accumulators.  Must be called by every wave of the workgroup (it has a
+// barrier when it stages), with no loads into the ring outstanding.
+template <class C, class ML>
+__device__ __forceinline__ void store_tile(ML& ml, const typename C::Acc (&acc)[C::FM][C::FN], void* dst,
+                                           int64_t ldc, int kind, bool vec_ok) {
+    constexpr int R = C::WTM * C::WTN * 2;  // bytes of one wave's staged sub-tile
+    constexpr int RB = C::WTN * 2;          // bytes per staged row
+    constexpr int CPR = RB / 16;            // 16-byte chunks per staged row
+    constexpr int MI = C::MI, NH = C::NH, NG = MI == 32 ? 4 : 1;
+    if constexpr (stage_pieces<C, R>() >= C::NW && CPR >= 2 && CPR <= 64 && (CPR & (CPR - 1)) == 0) {
+        const bool full = vec_ok && kind != OUT_F32 && ml.m0 + C::BM <= ml.p.M && ml.n0 + C::BN <= ml.p.N;
+        if (full) {
+            ring_barrier();  // every wave has finished reading the ring
+            IGC_LDS char* reg = stage_piece<C, R>(ml.wave);
+            const int lane = ml.lane;
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        const int row = MI * i + lane % MI;
+                        const int col = MI * j + 4 * NH * g + 4 * (lane / MI);
+                        const int chunk = (col >> 3) ^ (row & (CPR - 1));
+                        IGC_LDS char* a = reg + row * RB + chunk * 16 + (col & 7) * 2;
+                        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                        if (kind == OUT_BF16) {
+                            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+                            *(IGC_LDS bf16x4_t*)a = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                        } else {
+                            typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+                            *(IGC_LDS f16x4_t*)a = f16x4_t{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+                        }
+                    }
+            // the wave's own writes, read back by other lanes of the same wave
+            wait_lgkmcnt0();
+            compiler_fence();
+            typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+            constexpr int RPI = 64 / CPR;  // staged rows per read instruction
+            const int64_t gm0 = ml.m0 + ml.wm * C::WTM, gn0 = ml.n0 + ml.wn * C::WTN;
+#pragma unroll
+            for (int q = 0; q < C::WTM / RPI; ++q) {
+                const int row = q * RPI + lane / CPR, c = lane % CPR;
+                const u32x4_t v = *(const IGC_LDS u32x4_t*)(reg + row * RB + ((c ^ (row & (CPR - 1))) * 16));
+                *(u32x4_t*)((char*)dst + ((gm0 + row) * ldc + gn0 + 8 * c) * 2) = v;
+            }
+            return;
+        }
+    }
+    ml.store(acc, dst, ldc, kind, vec_ok);
+}
+
 // The K range [kbase, kend) of one output tile: setup, the K loop of variant
 // V, then epi(ml, acc) with the accumulators.
 template <class C, int V, bool LOADER, class Epi>
@@ -1062,7 +1143,7 @@ __device__ __forceinline__ void stream_k(const Params p) {
                     for (int gp = g - 1; gp >= 0 && sk_end(total, G, gp) > tile_start; --gp)
                         ml.sk_collect(acc, p.sk_ws + (int64_t)gp * (C::BM * C::BN), p.sk_flags + 2 * gp,
                                       p.sk_epoch);
-                    ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+                    store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
                 }
             });
         });
@@ -1089,7 +1170,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
             if (p.k_splits > 1)
                 ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
             else
-                ml.store(acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+                store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
         });
     });
 }

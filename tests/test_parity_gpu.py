@@ -413,3 +413,22 @@ def test_conv_1x1_equals_gemm_on_gpu():
     ref, S = oracle_gemm(N * H * W, K, C, x.reshape(-1, C), C, "row", w.reshape(K, C), C, "col")
     assert_close(yc.reshape(-1, K), ref, S, "f32", "1x1 conv")
     assert_close(yg, ref, S, "f32", "1x1 as gemm")
+
+
+@pytest.mark.parametrize("stream_k", [0, 3])
+@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
+def test_output_epilogue_exact(tune, stream_k):
+    """Full tiles with a 16-bit output go through the LDS-staged epilogue (whole row segments per store), the
+    others store from the accumulators: both kinds of tile in one call, with padding between N and ldc, must
+    equal the oracle rounded once to nearest-even (exact-integer inputs), and leave the padding untouched."""
+    bm, bn = tune[0], tune[1]
+    M, N, K = 2 * bm + 40, bn + 24, 136
+    for i, (dtype, out) in enumerate((("bf16", "bf16"), ("fp16", "f16"))):
+        A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", K, N, dtype, ("int", 4), ("int", 4),
+                                              seed=40 + i)
+        t = tuple(tune[:8]) + (1, stream_k)
+        say(f"epilogue {M}x{N}x{K} {dtype}->{out} tune={t}")
+        y, _ = run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out=out, dtype=dtype, ldc=N + 8, tune=t)
+        ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row", dtype)
+        bad = np.count_nonzero(y != round_to(ref, out))
+        assert bad == 0, f"{bad} outputs differ from the exactly rounded oracle"
