@@ -37,20 +37,21 @@ const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_
 }
 
 igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv) {
+    (void)conv;  // the GEMM and the convolution view take the same choice
     constexpr int64_t kCUs = 256;
     // Enough 256x256 tiles for every CU: the largest tile (least global and LDS
-    // traffic per flop), 8 waves.  GEMM: 64-deep K tiles (128-byte rows load
-    // faster) in a 2.5-stage ring, 16x16x32 MFMAs (which hold a higher clock
-    // than 32x32x16 under load), loads issued by one wave per SIMD.  Conv:
-    // 32-deep K tiles in a 4-stage ring with 32x32x16 MFMAs, every wave loading
-    // (measured fastest for its im2col address stream).
+    // traffic per flop), 8 waves, 32-deep K tiles in a 4-stage ring, 16x16x32
+    // MFMAs (which hold a higher clock than 32x32x16 under load) and loads
+    // issued by one wave per SIMD: measured fastest, by a small margin, for
+    // both the GEMM and the convolution once the output tile is stored
+    // through LDS.
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     // 256x256 tiles unless they pad the output by more than a third more than
     // 128x128 tiles do (a 64-wide N, say) while 128x128 still fills the CUs
     const bool wasteful = t256 * 65536 * 3 > t128 * 16384 * 4 && t128 >= kCUs;
     if (t256 >= kCUs && !wasteful)
-        return conv ? igc_tune_t{256, 256, 32, 4, 8, 32, 0, 8, 1, 0} : igc_tune_t{256, 256, 64, 2, 8, 16, 1, 4, 1, 0};
+        return igc_tune_t{256, 256, 32, 4, 8, 16, 0, 4, 1, 0};
     // Otherwise 128x128 tiles; when even those leave CUs idle and K is deep
     // (at least 2048 per CU's share), stream-K over every CU balances the K
     // work; shallow K runs one tile per workgroup.

@@ -155,9 +155,9 @@ def test_tune_table_fits_lds():
 
 
 @pytest.mark.parametrize("shape,conv,expect", [
-    ((8192, 8192, 8192), 0, ((256, 256, 64, 2, 8, 16, 1, 4), 1, 0)),   # 1024 tiles of 256x256: data-parallel
-    ((100352, 256, 2304), 1, ((256, 256, 32, 4, 8, 32, 0, 8), 1, 0)),  # the 3x3 conv's GEMM view
-    ((100352, 256, 2304), 0, ((256, 256, 64, 2, 8, 16, 1, 4), 1, 0)),  # the same shape as a GEMM
+    ((8192, 8192, 8192), 0, ((256, 256, 32, 4, 8, 16, 0, 4), 1, 0)),   # 1024 tiles of 256x256: data-parallel
+    ((100352, 256, 2304), 1, ((256, 256, 32, 4, 8, 16, 0, 4), 1, 0)),  # the 3x3 conv's GEMM view
+    ((100352, 256, 2304), 0, ((256, 256, 32, 4, 8, 16, 0, 4), 1, 0)),  # the same shape as a GEMM
     ((2048, 1024, 16384), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 128 tiles of 128x128: stream-K
     ((1000, 1000, 65536), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 64 tiles
     ((1000, 1000, 3000), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),    # too little K to share
