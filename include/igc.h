@@ -19,9 +19,12 @@
  *   process-wide call counter that tags stream-K flags); calls are
  *   thread-safe.  A call that splits K takes a temporary fp32 workspace
  *   (k_splits * M * N * 4 bytes, N rounded up to 4), and a stream-K call one
- *   of G * BM * BN * 4 bytes plus 8 bytes per workgroup, with hipMallocAsync on `stream`
- *   and releases it with hipFreeAsync on the same stream; no other call
- *   allocates.
+ *   of G * BM * BN * 4 bytes plus 8 bytes per workgroup, stream-ordered on
+ *   `stream` from a memory pool the library creates on the current device at
+ *   its first such call, and releases it with hipFreeAsync on the same stream;
+ *   no other call allocates.  The pool keeps up to 256 MiB of freed workspace
+ *   mapped for later calls until the process ends (the device's default pool
+ *   is not changed).  `stream` must belong to the current device.
  * - Each call only validates its arguments and enqueues work on `stream`
  *   (a hipStream_t; NULL = the default stream).  It returns before the GPU
  *   finishes; synchronise the stream to observe the result.
