@@ -418,12 +418,13 @@ def test_conv_1x1_equals_gemm_on_gpu():
 @pytest.mark.parametrize("stream_k", [0, 3])
 @pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
 def test_output_epilogue_exact(tune, stream_k):
-    """Full tiles with a 16-bit output go through the LDS-staged epilogue (whole row segments per store), the
-    others store from the accumulators: both kinds of tile in one call, with padding between N and ldc, must
-    equal the oracle rounded once to nearest-even (exact-integer inputs), and leave the padding untouched."""
+    """Full tiles with a 16-bit output go through the LDS-staged epilogue (whole row segments per store), edge
+    tiles and fp32 output store from the accumulators: every kind of tile in one call, with padding between N
+    and ldc, must equal the oracle rounded once to nearest-even (exact-integer inputs, so fp32 output is the
+    exact sum), and leave the padding untouched."""
     bm, bn = tune[0], tune[1]
     M, N, K = 2 * bm + 40, bn + 24, 136
-    for i, (dtype, out) in enumerate((("bf16", "bf16"), ("fp16", "f16"))):
+    for i, (dtype, out) in enumerate((("bf16", "bf16"), ("fp16", "f16"), ("bf16", "f32"))):
         A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", K, N, dtype, ("int", 4), ("int", 4),
                                               seed=40 + i)
         t = tuple(tune[:8]) + (1, stream_k)
