@@ -864,61 +864,85 @@ __device__ __forceinline__ IGC_LDS char* stage_piece(int w) {
     }
 }
 
-// Output epilogue.  A full tile with a 2-byte output type goes through LDS:
-// after the ring's last reads, each wave writes its WTM x WTN sub-tile,
-// converted, into a private piece of the ring (16-byte chunks of a row
-// XOR-swizzled by the row, so the 2-byte-column writes of an MFMA block spread
-// over the banks), reads it back 16 bytes per lane and stores whole row
-// segments: every store instruction writes WTN*2-byte runs of consecutive
-// addresses instead of 8-byte pieces of 16 or 32 rows, which the memory system
-// retires far faster.  Other tiles and fp32 output store straight from the
-// accumulators.  Must be called by every wave of the workgroup (it has a
+// Chunk swizzle of a staged row of CPR 16-byte chunks.  Rows of 256 bytes or
+// more start on the same bank, so the row itself spreads them; 128-byte rows
+// alternate between the two bank halves with the row's parity, so row/2
+// spreads each half.  Either way the 16 (or 32) rows an MFMA block writes at
+// one column land on distinct banks, and every read of whole rows is
+// conflict-free.
+template <int CPR>
+__device__ __forceinline__ int stage_swz(int row) {
+    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "staged rows of 128 bytes or more");
+    return CPR >= 16 ? (row & (CPR - 1)) : ((row >> 1) & (CPR - 1));
+}
+
+// Blocks I0 .. I0+NI-1 (MFMA block rows) of a wave's sub-tile, as ESZ-byte
+// elements: written into the wave's LDS piece `reg` (row-major, swizzled
+// chunks), read back 16 bytes per lane and stored as whole row segments.
+template <class C, int ESZ, int I0, int NI, class ML>
+__device__ __forceinline__ void stage_rows(ML& ml, const typename C::Acc (&acc)[C::FM][C::FN], IGC_LDS char* reg,
+                                           void* dst, int64_t ldc, int kind) {
+    constexpr int MI = C::MI, NH = C::NH, NG = MI == 32 ? 4 : 1;
+    constexpr int RB = C::WTN * ESZ;  // bytes per staged row
+    constexpr int CPR = RB / 16;      // 16-byte chunks per staged row
+    const int lane = ml.lane;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int row = MI * i + lane % MI;
+                const int byte = (MI * j + 4 * NH * g + 4 * (lane / MI)) * ESZ;
+                IGC_LDS char* a = reg + row * RB + (((byte >> 4) ^ stage_swz<CPR>(row)) << 4) + (byte & 15);
+                const float v0 = acc[I0 + i][j][4 * g + 0], v1 = acc[I0 + i][j][4 * g + 1];
+                const float v2 = acc[I0 + i][j][4 * g + 2], v3 = acc[I0 + i][j][4 * g + 3];
+                if constexpr (ESZ == 4) {
+                    *(IGC_LDS f32x4_t*)a = f32x4_t{v0, v1, v2, v3};
+                } else if (kind == OUT_BF16) {
+                    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+                    *(IGC_LDS bf16x4_t*)a = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                } else {
+                    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+                    *(IGC_LDS f16x4_t*)a = f16x4_t{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+                }
+            }
+    // the wave's own writes, read back by other lanes of the same wave
+    wait_lgkmcnt0();
+    compiler_fence();
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+    constexpr int RPI = 64 / CPR;  // staged rows per read instruction
+    const int64_t gm0 = ml.m0 + ml.wm * C::WTM + MI * I0, gn0 = ml.n0 + ml.wn * C::WTN;
+#pragma unroll
+    for (int q = 0; q < NI * MI / RPI; ++q) {
+        const int row = q * RPI + lane / CPR, c = lane % CPR;
+        const u32x4_t v = *(const IGC_LDS u32x4_t*)(reg + row * RB + ((c ^ stage_swz<CPR>(row)) << 4));
+        *(u32x4_t*)((char*)dst + ((gm0 + row) * ldc + gn0) * ESZ + c * 16) = v;
+    }
+    // reads done before the piece is written again
+    wait_lgkmcnt0();
+    compiler_fence();
+}
+
+// Output epilogue.  A full tile goes through LDS: after the ring's last reads,
+// each wave writes its WTM x WTN sub-tile, converted, into a private piece of
+// the drained ring, reads it back 16 bytes per lane and stores whole row
+// segments, so every store instruction writes runs of consecutive addresses
+// (whole 128-byte lines) instead of 8- or 16-byte pieces of 16 or 32 rows,
+// which the memory system retires far faster.  Edge tiles and fp32 output
+// store straight from the accumulators (staging fp32 as two passes of
+// stage_rows<C, 4, ...> raised the register pressure of the whole kernel until
+// its K loop spilled).  Must be called by every wave of the workgroup (it has a
 // barrier when it stages), with no loads into the ring outstanding.
 template <class C, class ML>
 __device__ __forceinline__ void store_tile(ML& ml, const typename C::Acc (&acc)[C::FM][C::FN], void* dst,
                                            int64_t ldc, int kind, bool vec_ok) {
-    constexpr int R = C::WTM * C::WTN * 2;  // bytes of one wave's staged sub-tile
-    constexpr int RB = C::WTN * 2;          // bytes per staged row
-    constexpr int CPR = RB / 16;            // 16-byte chunks per staged row
-    constexpr int MI = C::MI, NH = C::NH, NG = MI == 32 ? 4 : 1;
-    if constexpr (stage_pieces<C, R>() >= C::NW && CPR >= 2 && CPR <= 64 && (CPR & (CPR - 1)) == 0) {
+    constexpr int R = C::WTM * C::WTN * 2;  // bytes of one wave's LDS piece
+    if constexpr (stage_pieces<C, R>() >= C::NW && C::WTN * 2 >= 128) {
         const bool full = vec_ok && kind != OUT_F32 && ml.m0 + C::BM <= ml.p.M && ml.n0 + C::BN <= ml.p.N;
         if (full) {
             ring_barrier();  // every wave has finished reading the ring
-            IGC_LDS char* reg = stage_piece<C, R>(ml.wave);
-            const int lane = ml.lane;
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) {
-                        const int row = MI * i + lane % MI;
-                        const int col = MI * j + 4 * NH * g + 4 * (lane / MI);
-                        const int chunk = (col >> 3) ^ (row & (CPR - 1));
-                        IGC_LDS char* a = reg + row * RB + chunk * 16 + (col & 7) * 2;
-                        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                        if (kind == OUT_BF16) {
-                            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-                            *(IGC_LDS bf16x4_t*)a = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                        } else {
-                            typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
-                            *(IGC_LDS f16x4_t*)a = f16x4_t{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-                        }
-                    }
-            // the wave's own writes, read back by other lanes of the same wave
-            wait_lgkmcnt0();
-            compiler_fence();
-            typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
-            constexpr int RPI = 64 / CPR;  // staged rows per read instruction
-            const int64_t gm0 = ml.m0 + ml.wm * C::WTM, gn0 = ml.n0 + ml.wn * C::WTN;
-#pragma unroll
-            for (int q = 0; q < C::WTM / RPI; ++q) {
-                const int row = q * RPI + lane / CPR, c = lane % CPR;
-                const u32x4_t v = *(const IGC_LDS u32x4_t*)(reg + row * RB + ((c ^ (row & (CPR - 1))) * 16));
-                *(u32x4_t*)((char*)dst + ((gm0 + row) * ldc + gn0 + 8 * c) * 2) = v;
-            }
+            stage_rows<C, 2, 0, C::FM>(ml, acc, stage_piece<C, R>(ml.wave), dst, ldc, kind);
             return;
         }
     }
