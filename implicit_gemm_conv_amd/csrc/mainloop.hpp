@@ -972,6 +972,11 @@ template <class C, int V, bool LOADER, class Epi>
 __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int64_t kbase, int64_t kend, Epi&& epi) {
     using ML = Mainloop<C, V, LOADER>;
     constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN, U = C::U, P = C::P;
+    // A loading wave shares its SIMD with a compute-only wave; issuing its
+    // instructions first keeps the loads of the ring going out on time (the
+    // compute-only wave's MFMAs fill the gaps).  Measured: 1.5% off the GEMM
+    // and 3% off the conv; the opposite priority costs 13%.
+    if constexpr (LOADER && C::NL != C::NW) __builtin_amdgcn_s_setprio(2);
     ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN, kbase, kend);
     const int KT = ml.KT, KTp = ml.KTp;
 
