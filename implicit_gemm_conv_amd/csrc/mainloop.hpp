@@ -973,10 +973,12 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
     using ML = Mainloop<C, V, LOADER>;
     constexpr int D = C::D, KK = C::KK, FM = C::FM, FN = C::FN, U = C::U, P = C::P;
     // A loading wave shares its SIMD with a compute-only wave; issuing its
-    // instructions first keeps the loads of the ring going out on time (the
-    // compute-only wave's MFMAs fill the gaps).  Measured: 1.5% off the GEMM
-    // and 3% off the conv; the opposite priority costs 13%.
-    if constexpr (LOADER && C::NL != C::NW) __builtin_amdgcn_s_setprio(2);
+    // instructions first keeps the loads of whole-stage rings going out on
+    // time (the compute-only wave's MFMAs fill the gaps).  Measured on the
+    // 4-stage 32-deep ring: 1.5% off the GEMM and 3% off the conv (the
+    // opposite priority costs 13%); on the 2.5-stage ring, whose refills are
+    // already spread through the MFMAs, it slowed the conv by 30%.
+    if constexpr (LOADER && C::NL != C::NW && C::HALF == 0) __builtin_amdgcn_s_setprio(2);
     ML ml(p, (int64_t)tm * C::BM, (int64_t)tn * C::BN, kbase, kend);
     const int KT = ml.KT, KTp = ml.KTp;
 
