@@ -11,6 +11,10 @@ input bits (igc_oracle.c states the formulas and the passages they follow):
 * gemm_sample(...)        -> (c, s)  selected (row, col) outputs only
 * conv2d_nhwc(...)        -> (y, S)  direct convolution, every output
 * conv2d_nhwc_sample(...) -> (y, s)  selected flat NPQK outputs only
+* conv2d_dgrad_nhwc(...)  -> (dx, S) data gradient (NHWC) from dy (NPQK) and w (KRSC)
+* conv2d_dgrad_nhwc_sample(...)     selected flat NHWC dx outputs only
+* conv2d_wgrad_nhwc(...)  -> (dw, S) filter gradient (KRSC) from x (NHWC) and dy (NPQK)
+* conv2d_wgrad_nhwc_sample(...)     selected flat KRSC dw outputs only
 * decode(bits, dtype)     -> exact float64 value of one bf16/fp16 pattern
 
 S is sum |a*b| over the same terms; it scales the error bound.  After each
@@ -63,6 +67,12 @@ class Oracle:
         lib.oracle_conv2d_nhwc.restype = i32
         lib.oracle_conv2d_nhwc_sample.argtypes = [i64] * 13 + [p, p, i32, i64, p, p, p, i32]
         lib.oracle_conv2d_nhwc_sample.restype = i32
+        for name in ("oracle_conv2d_dgrad_nhwc", "oracle_conv2d_wgrad_nhwc"):
+            getattr(lib, name).argtypes = [i64] * 13 + [p, p, i32, p, p, i32]
+            getattr(lib, name).restype = i32
+        for name in ("oracle_conv2d_dgrad_nhwc_sample", "oracle_conv2d_wgrad_nhwc_sample"):
+            getattr(lib, name).argtypes = [i64] * 13 + [p, p, i32, i64, p, p, p, i32]
+            getattr(lib, name).restype = i32
         self.lib = lib
         self.last_threads = 0
 
@@ -114,6 +124,47 @@ class Oracle:
         return y, ys
 
 
+    def conv2d_dgrad_nhwc(self, N, H, W, C, K, R, S, dy, w, dtype, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, threads=0):
+        """dx[N, H, W, C] and its |.|-sum from dy[N, P, Q, K] and w[K, R, S, C] (bit arrays)."""
+        dy, w = _bits(dy), _bits(w)
+        dx = np.empty((N, H, W, C), np.float64)
+        dxs = np.empty((N, H, W, C), np.float64)
+        self._check(self.lib.oracle_conv2d_dgrad_nhwc(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, _ptr(dy), _ptr(w),
+                                                      dtype, _ptr(dx), _ptr(dxs), threads))
+        return dx, dxs
+
+    def conv2d_dgrad_nhwc_sample(self, N, H, W, C, K, R, S, dy, w, dtype, idx, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1,
+                                 threads=0):
+        dy, w = _bits(dy), _bits(w)
+        idx = np.ascontiguousarray(idx, np.int64)
+        v = np.empty(idx.shape, np.float64)
+        vs = np.empty(idx.shape, np.float64)
+        self._check(self.lib.oracle_conv2d_dgrad_nhwc_sample(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, _ptr(dy),
+                                                             _ptr(w), dtype, idx.size, _ptr(idx), _ptr(v), _ptr(vs),
+                                                             threads))
+        return v, vs
+
+    def conv2d_wgrad_nhwc(self, N, H, W, C, K, R, S, x, dy, dtype, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, threads=0):
+        """dw[K, R, S, C] and its |.|-sum from x[N, H, W, C] and dy[N, P, Q, K] (bit arrays)."""
+        x, dy = _bits(x), _bits(dy)
+        g = np.empty((K, R, S, C), np.float64)
+        gs = np.empty((K, R, S, C), np.float64)
+        self._check(self.lib.oracle_conv2d_wgrad_nhwc(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, _ptr(x), _ptr(dy),
+                                                      dtype, _ptr(g), _ptr(gs), threads))
+        return g, gs
+
+    def conv2d_wgrad_nhwc_sample(self, N, H, W, C, K, R, S, x, dy, dtype, idx, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1,
+                                 threads=0):
+        x, dy = _bits(x), _bits(dy)
+        idx = np.ascontiguousarray(idx, np.int64)
+        v = np.empty(idx.shape, np.float64)
+        vs = np.empty(idx.shape, np.float64)
+        self._check(self.lib.oracle_conv2d_wgrad_nhwc_sample(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, _ptr(x),
+                                                             _ptr(dy), dtype, idx.size, _ptr(idx), _ptr(v), _ptr(vs),
+                                                             threads))
+        return v, vs
+
+
 _default = None
 
 
@@ -149,3 +200,19 @@ def conv2d_nhwc_sample(*a, **k):
 
 def last_threads():
     return default().last_threads
+
+
+def conv2d_dgrad_nhwc(*a, **k):
+    return default().conv2d_dgrad_nhwc(*a, **k)
+
+
+def conv2d_dgrad_nhwc_sample(*a, **k):
+    return default().conv2d_dgrad_nhwc_sample(*a, **k)
+
+
+def conv2d_wgrad_nhwc(*a, **k):
+    return default().conv2d_wgrad_nhwc(*a, **k)
+
+
+def conv2d_wgrad_nhwc_sample(*a, **k):
+    return default().conv2d_wgrad_nhwc_sample(*a, **k)

@@ -25,13 +25,30 @@
  *          implicit GEMM with IM2COL loads (section "The atom changes the
  *          fragment"); cross-correlation, forward only.
  *
+ *   DGRAD  dx[n][h][w][c] = sum over (r, s, k) of dy[n][p][q][k] * wt[k][r][s][c],
+ *          over the filter taps at which the forward convolution reads
+ *          x[n][h][w]: p*sh - ph + r*dh = h and q*sw - pw + s*dw = w for
+ *          integers 0 <= p < P, 0 <= q < Q.  This is the derivative of
+ *          sum(y * dy) with respect to x, i.e. the adjoint of the forward
+ *          convolution in x.  dy is NPQK, dx is NHWC.
+ *
+ *   WGRAD  dw[k][r][s][c] = sum over (n, p, q) of dy[n][p][q][k] * x[n][h][w][c],
+ *          h = p*sh - ph + r*dh, w = q*sw - pw + s*dw, terms outside the
+ *          image omitted: the derivative of sum(y * dy) with respect to the
+ *          filter, the adjoint of the forward convolution in wt.  dw is KRSC.
+ *          Both gradients run on the same implicit-GEMM mainloop as the
+ *          forward pass (the "two free pipeline stages" note runs the forward
+ *          convolution through it; the data and filter gradients are the two
+ *          other convolutions of a training step).
+ *
  *   Each output also gets its absolute-product sum S = sum |a*b| (same index
  *   set), which scales the error bound |y - C| <= 1e-4*S + 1e-6.
  *
  * How: every stored 16-bit input is decoded exactly to double, every product
  * of two bf16 or two fp16 values is exact in double, and each output's sum is
  * taken sequentially in increasing k (GEMM) or in (r, s, c) order (conv) in
- * double.  Threads split the OUTPUT rows only, so the result does not depend
+ * double (dgrad in (r, s, k) order, wgrad in (n, p, q) order).  Threads split
+ * the OUTPUT elements only, so the result does not depend
  * on the thread count.  No fast-math.
  *
  * dtype: 0 = bfloat16 bits, 1 = IEEE binary16 bits.
@@ -214,7 +231,7 @@ int oracle_gemm_sample(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64
 typedef struct {
     int64_t N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, P, Q;
     int dtype;
-    const uint16_t *x, *w;
+    const uint16_t *x, *w, *dy; /* forward input, filter, output gradient (NPQK) */
     /* either a contiguous range of output pixels (flat n*P*Q index) ... */
     int64_t pix0, pix1;
     double *y, *ys;
@@ -323,4 +340,168 @@ int oracle_conv2d_nhwc_sample(int64_t N, int64_t H, int64_t W, int64_t C, int64_
     }
     run_threads(n, conv_points, jobs, sizeof(conv_job));
     return n;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Data gradient: dx (NHWC) from dy (NPQK) and the filter (KRSC)              */
+/* ------------------------------------------------------------------------- */
+
+/* One dx element: every (r, s, k) whose forward tap lands on (h, w). */
+static void dgrad_point(const conv_job *jb, int64_t n, int64_t h, int64_t w, int64_t c, double *out,
+                        double *outs) {
+    double acc = 0.0, sacc = 0.0;
+    for (int64_t r = 0; r < jb->R; r++) {
+        const int64_t pnum = h + jb->ph - r * jb->dh; /* = p * sh */
+        if (pnum < 0 || pnum % jb->sh != 0) continue;
+        const int64_t p = pnum / jb->sh;
+        if (p >= jb->P) continue;
+        for (int64_t s = 0; s < jb->S; s++) {
+            const int64_t qnum = w + jb->pw - s * jb->dw; /* = q * sw */
+            if (qnum < 0 || qnum % jb->sw != 0) continue;
+            const int64_t q = qnum / jb->sw;
+            if (q >= jb->Q) continue;
+            const uint16_t *dyp = jb->dy + ((n * jb->P + p) * jb->Q + q) * jb->K;
+            for (int64_t k = 0; k < jb->K; k++) {
+                const double prod = dec(dyp[k], jb->dtype) * dec(jb->w[((k * jb->R + r) * jb->S + s) * jb->C + c], jb->dtype);
+                acc += prod;
+                sacc += fabs(prod);
+            }
+        }
+    }
+    *out = acc;
+    *outs = sacc;
+}
+
+static void *dgrad_pixels(void *p) {
+    conv_job *jb = (conv_job *)p;
+    for (int64_t pix = jb->pix0; pix < jb->pix1; pix++) {
+        const int64_t n = pix / (jb->H * jb->W), hw = pix % (jb->H * jb->W);
+        const int64_t h = hw / jb->W, w = hw % jb->W;
+        for (int64_t c = 0; c < jb->C; c++) dgrad_point(jb, n, h, w, c, &jb->y[pix * jb->C + c], &jb->ys[pix * jb->C + c]);
+    }
+    return NULL;
+}
+
+static void *dgrad_points(void *p) {
+    conv_job *jb = (conv_job *)p;
+    for (int64_t t = jb->i0; t < jb->i1; t++) {
+        int64_t f = jb->idx[t];
+        const int64_t c = f % jb->C; f /= jb->C;
+        const int64_t w = f % jb->W; f /= jb->W;
+        const int64_t h = f % jb->H; f /= jb->H;
+        dgrad_point(jb, f, h, w, c, &jb->y[t], &jb->ys[t]);
+    }
+    return NULL;
+}
+
+int oracle_conv2d_dgrad_nhwc(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S, int64_t sh,
+                             int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, const uint16_t *dy,
+                             const uint16_t *w, int dtype, double *dx, double *dxs, int nthreads) {
+    conv_job base;
+    if (conv_setup(&base, N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, NULL, w, dtype) != 0) return OR_EINVAL;
+    base.dy = dy;
+    const int64_t npix = N * H * W;
+    if (npix * C > 0 && (!dx || !dxs)) return OR_EINVAL;
+    if (npix > 0 && C > 0 && K > 0 && (!dy || !w)) return OR_EINVAL;
+    int n = pick_threads(nthreads, npix);
+    conv_job jobs[256];
+    for (int t = 0; t < n; t++) {
+        jobs[t] = base;
+        jobs[t].pix0 = npix * t / n; jobs[t].pix1 = npix * (t + 1) / n;
+        jobs[t].y = dx; jobs[t].ys = dxs;
+    }
+    run_threads(n, dgrad_pixels, jobs, sizeof(conv_job));
+    return n;
+}
+
+int oracle_conv2d_dgrad_nhwc_sample(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                                    int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                                    const uint16_t *dy, const uint16_t *w, int dtype, int64_t nsamp,
+                                    const int64_t *idx, double *dx, double *dxs, int nthreads) {
+    conv_job base;
+    if (conv_setup(&base, N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, NULL, w, dtype) != 0) return OR_EINVAL;
+    base.dy = dy;
+    if (nsamp < 0 || (nsamp > 0 && (!idx || !dx || !dxs))) return OR_EINVAL;
+    const int64_t total = N * H * W * C;
+    for (int64_t t = 0; t < nsamp; t++)
+        if (idx[t] < 0 || idx[t] >= total) return OR_EINVAL;
+    if (nsamp > 0 && K > 0 && (!dy || !w)) return OR_EINVAL;
+    int n = pick_threads(nthreads, nsamp);
+    conv_job jobs[256];
+    for (int t = 0; t < n; t++) {
+        jobs[t] = base;
+        jobs[t].idx = idx; jobs[t].i0 = nsamp * t / n; jobs[t].i1 = nsamp * (t + 1) / n;
+        jobs[t].y = dx; jobs[t].ys = dxs;
+    }
+    run_threads(n, dgrad_points, jobs, sizeof(conv_job));
+    return n;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Filter gradient: dw (KRSC) from x (NHWC) and dy (NPQK)                     */
+/* ------------------------------------------------------------------------- */
+
+/* One dw element: every output pixel (n, p, q) whose window puts tap (r, s) inside the image. */
+static void wgrad_point(const conv_job *jb, int64_t k, int64_t r, int64_t s, int64_t c, double *out, double *outs) {
+    double acc = 0.0, sacc = 0.0;
+    for (int64_t n = 0; n < jb->N; n++)
+        for (int64_t p = 0; p < jb->P; p++) {
+            const int64_t h = p * jb->sh - jb->ph + r * jb->dh;
+            if (h < 0 || h >= jb->H) continue;
+            for (int64_t q = 0; q < jb->Q; q++) {
+                const int64_t w = q * jb->sw - jb->pw + s * jb->dw;
+                if (w < 0 || w >= jb->W) continue;
+                const double prod = dec(jb->dy[((n * jb->P + p) * jb->Q + q) * jb->K + k], jb->dtype) *
+                                    dec(jb->x[((n * jb->H + h) * jb->W + w) * jb->C + c], jb->dtype);
+                acc += prod;
+                sacc += fabs(prod);
+            }
+        }
+    *out = acc;
+    *outs = sacc;
+}
+
+static void *wgrad_points(void *p) {
+    conv_job *jb = (conv_job *)p;
+    for (int64_t t = jb->i0; t < jb->i1; t++) {
+        int64_t f = jb->idx ? jb->idx[t] : t;
+        const int64_t c = f % jb->C; f /= jb->C;
+        const int64_t s = f % jb->S; f /= jb->S;
+        const int64_t r = f % jb->R; f /= jb->R;
+        wgrad_point(jb, f, r, s, c, &jb->y[t], &jb->ys[t]);
+    }
+    return NULL;
+}
+
+/* idx == NULL: every element, in KRSC order (nsamp must be K*R*S*C). */
+int oracle_conv2d_wgrad_nhwc_sample(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                                    int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                                    const uint16_t *x, const uint16_t *dy, int dtype, int64_t nsamp,
+                                    const int64_t *idx, double *dwt, double *dws, int nthreads) {
+    conv_job base;
+    if (conv_setup(&base, N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, x, NULL, dtype) != 0) return OR_EINVAL;
+    base.dy = dy;
+    const int64_t total = K * R * S * C;
+    if (nsamp < 0 || (nsamp > 0 && (!dwt || !dws)) || (!idx && nsamp != total)) return OR_EINVAL;
+    if (idx)
+        for (int64_t t = 0; t < nsamp; t++)
+            if (idx[t] < 0 || idx[t] >= total) return OR_EINVAL;
+    if (nsamp > 0 && N * base.P * base.Q > 0 && (!x || !dy)) return OR_EINVAL;
+    int n = pick_threads(nthreads, nsamp);
+    conv_job jobs[256];
+    for (int t = 0; t < n; t++) {
+        jobs[t] = base;
+        jobs[t].idx = idx; jobs[t].i0 = nsamp * t / n; jobs[t].i1 = nsamp * (t + 1) / n;
+        jobs[t].y = dwt; jobs[t].ys = dws;
+    }
+    run_threads(n, wgrad_points, jobs, sizeof(conv_job));
+    return n;
+}
+
+int oracle_conv2d_wgrad_nhwc(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S, int64_t sh,
+                             int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw, const uint16_t *x,
+                             const uint16_t *dy, int dtype, double *dwt, double *dws, int nthreads) {
+    if (K < 0 || R < 1 || S < 1 || C < 0) return OR_EINVAL;
+    return oracle_conv2d_wgrad_nhwc_sample(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, x, dy, dtype, K * R * S * C,
+                                           NULL, dwt, dws, nthreads);
 }

@@ -16,6 +16,10 @@ What pins what:
   sum that changes if a K block is dropped, repeated or read stale;
 * convolution special cases: 1x1 filter equals the GEMM oracle, a delta
   filter reproduces x, all-ones operands count the in-bounds taps;
+* convolution gradients: torch's own gradient routines in float64, the
+  adjoint identity <dy, conv(x, w)> = <dgrad(dy, w), x> = <wgrad(x, dy), w>
+  in exact integer arithmetic, the 1x1 case equal to the GEMM oracle
+  bit-for-bit, and hand-worked gradients;
 * hand-worked fixtures under tests/golden/;
 * sampled entry points agree bit-for-bit with the full ones.
 """
@@ -390,9 +394,142 @@ def pin_conv_sample_consistency(orc):
     return True, "ok"
 
 
+# ----------------------------------------------------------------------------
+# convolution gradient pins
+# ----------------------------------------------------------------------------
+
+GRAD_SHAPES = [
+    # N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw
+    (2, 7, 9, 8, 5, 3, 3, 1, 1, 1, 1, 1, 1),
+    (1, 8, 6, 16, 4, 3, 3, 2, 2, 1, 1, 1, 1),     # stride 2: dx pixels with no tap, others with one
+    (1, 9, 10, 8, 6, 3, 2, 3, 2, 2, 1, 2, 1),     # stride 3 x 2, dilation, asymmetric filter
+    (2, 5, 5, 8, 3, 3, 3, 1, 1, 0, 0, 1, 1),      # no padding: border pixels see fewer taps
+    (1, 7, 9, 8, 4, 2, 3, 2, 1, 1, 2, 1, 2),
+    (3, 1, 2, 8, 7, 3, 3, 1, 1, 1, 1, 1, 1),      # tiny image
+]
+
+
+def _torch_grads(x, w, dy, sh, sw, ph, pw, dh, dw):
+    """NHWC x, KRSC w, NPQK dy (float64 numpy) -> (dx NHWC, dw KRSC) by torch.nn.grad on NCHW / KCRS permutes."""
+    xt = torch.from_numpy(x).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(w).permute(0, 3, 1, 2)
+    gt = torch.from_numpy(dy).permute(0, 3, 1, 2)
+    gx = torch.nn.grad.conv2d_input(xt.shape, wt, gt, stride=(sh, sw), padding=(ph, pw), dilation=(dh, dw))
+    gw = torch.nn.grad.conv2d_weight(xt, wt.shape, gt, stride=(sh, sw), padding=(ph, pw), dilation=(dh, dw))
+    return gx.permute(0, 2, 3, 1).contiguous().numpy(), gw.permute(0, 2, 3, 1).contiguous().numpy()
+
+
+def pin_grad_torch(orc):
+    """dgrad and wgrad against torch's own convolution-gradient routines in float64 (independent code)."""
+    rng = np.random.default_rng(31)
+    for (N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw) in GRAD_SHAPES:
+        P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+        Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+        for dtype in (BF16, FP16):
+            xb = rand_bits(rng, (N, H, W, C), dtype)
+            wb = rand_bits(rng, (K, R, S, C), dtype, 0.1)
+            gb = rand_bits(rng, (N, P, Q, K), dtype)
+            x, w, g = np_decode(xb, dtype), np_decode(wb, dtype), np_decode(gb, dtype)
+            rdx, rdw = _torch_grads(x, w, g, sh, sw, ph, pw, dh, dw)
+            sdx, sdw = _torch_grads(np.abs(x), np.abs(w), np.abs(g), sh, sw, ph, pw, dh, dw)
+            dx, dxs = orc.conv2d_dgrad_nhwc(N, H, W, C, K, R, S, gb, wb, dtype, sh, sw, ph, pw, dh, dw)
+            gw, gws = orc.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, xb, gb, dtype, sh, sw, ph, pw, dh, dw)
+            shape = (N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw)
+            if dx.shape != rdx.shape or gw.shape != rdw.shape:
+                return _fail(f"gradient shapes {dx.shape} {gw.shape} vs {rdx.shape} {rdw.shape}")
+            if not (np.all(np.abs(dx - rdx) <= 1e-12 * sdx + 1e-300) and np.all(np.abs(dxs - sdx) <= 1e-12 * sdx)):
+                return _fail(f"dgrad vs torch {shape} dtype={dtype}")
+            if not (np.all(np.abs(gw - rdw) <= 1e-12 * sdw + 1e-300) and np.all(np.abs(gws - sdw) <= 1e-12 * sdw)):
+                return _fail(f"wgrad vs torch {shape} dtype={dtype}")
+    return True, "ok"
+
+
+def pin_grad_adjoint(orc):
+    """<dy, conv(x, w)> = <dgrad(dy, w), x> = <wgrad(x, dy), w>: the gradients are the adjoints of the forward
+    convolution in x and in w.  Small integers keep every product and sum exact in double, so the three inner
+    products must be equal exactly."""
+    rng = np.random.default_rng(32)
+    for (N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw) in GRAD_SHAPES:
+        P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+        Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+        xb = np_encode(rng.integers(-3, 4, (N, H, W, C)), BF16)
+        wb = np_encode(rng.integers(-3, 4, (K, R, S, C)), BF16)
+        gb = np_encode(rng.integers(-3, 4, (N, P, Q, K)), BF16)
+        y, _ = orc.conv2d_nhwc(N, H, W, C, K, R, S, xb, wb, BF16, sh, sw, ph, pw, dh, dw)
+        dx, _ = orc.conv2d_dgrad_nhwc(N, H, W, C, K, R, S, gb, wb, BF16, sh, sw, ph, pw, dh, dw)
+        gw, _ = orc.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, xb, gb, BF16, sh, sw, ph, pw, dh, dw)
+        a = float(np.sum(np_decode(gb, BF16) * y))
+        b = float(np.sum(dx * np_decode(xb, BF16)))
+        c = float(np.sum(gw * np_decode(wb, BF16)))
+        if not (a == b == c):
+            return _fail(f"adjoint identity {(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw)}: {a} {b} {c}")
+    return True, "ok"
+
+
+def pin_grad_1x1_is_gemm(orc):
+    """1x1 filter, stride 1, pad 0: dx = dy W with dy as [NHW x K] and W = w as [K x C] row-major, and
+    dw = dy^T x (dy read column-major); both gradients sum in the GEMM's k order, so the bits agree."""
+    rng = np.random.default_rng(33)
+    N, H, W, C, K = 2, 5, 7, 24, 16
+    xb = rand_bits(rng, (N, H, W, C), BF16)
+    wb = rand_bits(rng, (K, 1, 1, C), BF16)
+    gb = rand_bits(rng, (N, H, W, K), BF16)
+    dx, dxs = orc.conv2d_dgrad_nhwc(N, H, W, C, K, 1, 1, gb, wb, BF16)
+    Cg, Sg = orc.gemm(N * H * W, C, K, gb.reshape(-1, K), K, ROW_MAJOR, wb.reshape(K, C), C, ROW_MAJOR, BF16)
+    if not (np.array_equal(dx.reshape(-1, C), Cg) and np.array_equal(dxs.reshape(-1, C), Sg)):
+        return _fail("1x1 dgrad != gemm")
+    gw, gws = orc.conv2d_wgrad_nhwc(N, H, W, C, K, 1, 1, xb, gb, BF16)
+    Cw, Sw = orc.gemm(K, C, N * H * W, gb.reshape(-1, K), K, COL_MAJOR, xb.reshape(-1, C), C, ROW_MAJOR, BF16)
+    if not (np.array_equal(gw.reshape(K, C), Cw) and np.array_equal(gws.reshape(K, C), Sw)):
+        return _fail("1x1 wgrad != gemm")
+    return True, "ok"
+
+
+def pin_grad_golden(orc):
+    """Hand-worked gradients (tests/golden/conv_grads_by_hand.json)."""
+    with open(os.path.join(GOLDEN, "conv_grads_by_hand.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        H, W, R, S = c["H"], c["W"], c["R"], c["S"]
+        geo = (c["sh"], c["sw"], c["ph"], c["pw"], 1, 1)
+        x = np_encode(np.array(c["x"], np.float64).reshape(1, H, W, 1), BF16)
+        w = np_encode(np.array(c["w"], np.float64).reshape(1, R, S, 1), BF16)
+        dyv = np.array(c["dy"], np.float64)
+        dy = np_encode(dyv.reshape(1, dyv.shape[0], dyv.shape[1], 1), BF16)
+        dx, _ = orc.conv2d_dgrad_nhwc(1, H, W, 1, 1, R, S, dy, w, BF16, *geo)
+        dw, _ = orc.conv2d_wgrad_nhwc(1, H, W, 1, 1, R, S, x, dy, BF16, *geo)
+        if not np.array_equal(dx[0, :, :, 0], np.array(c["dx"], np.float64)):
+            return _fail(f"golden dgrad {c['name']}: {dx[0, :, :, 0].tolist()}")
+        if not np.array_equal(dw[0, :, :, 0], np.array(c["dw"], np.float64)):
+            return _fail(f"golden wgrad {c['name']}: {dw[0, :, :, 0].tolist()}")
+    return True, "ok"
+
+
+def pin_grad_sample_consistency(orc):
+    rng = np.random.default_rng(34)
+    N, H, W, C, K, R, S, sh, sw, ph, pw = 2, 7, 6, 16, 8, 3, 3, 2, 1, 1, 1
+    P = (H + 2 * ph - (R - 1) - 1) // sh + 1
+    Q = (W + 2 * pw - (S - 1) - 1) // sw + 1
+    xb = rand_bits(rng, (N, H, W, C), BF16)
+    wb = rand_bits(rng, (K, R, S, C), BF16)
+    gb = rand_bits(rng, (N, P, Q, K), BF16)
+    dx, dxs = orc.conv2d_dgrad_nhwc(N, H, W, C, K, R, S, gb, wb, BF16, sh, sw, ph, pw)
+    idx = rng.integers(0, dx.size, 200)
+    v, vs = orc.conv2d_dgrad_nhwc_sample(N, H, W, C, K, R, S, gb, wb, BF16, idx, sh, sw, ph, pw)
+    if not (np.array_equal(v, dx.ravel()[idx]) and np.array_equal(vs, dxs.ravel()[idx])):
+        return _fail("dgrad sample != full")
+    gw, gws = orc.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, xb, gb, BF16, sh, sw, ph, pw)
+    idx = rng.integers(0, gw.size, 200)
+    v, vs = orc.conv2d_wgrad_nhwc_sample(N, H, W, C, K, R, S, xb, gb, BF16, idx, sh, sw, ph, pw)
+    if not (np.array_equal(v, gw.ravel()[idx]) and np.array_equal(vs, gws.ravel()[idx])):
+        return _fail("wgrad sample != full")
+    return True, "ok"
+
+
 ALL_PINS = [
     pin_decode_exhaustive, pin_identity_permutation, pin_rank1, pin_bruteforce_fraction, pin_torch_matmul,
     pin_k_chain, pin_degenerate, pin_golden_gemm, pin_gemm_sample_consistency,
     pin_conv_torch, pin_conv_1x1_is_gemm, pin_conv_delta, pin_conv_ones_counts, pin_conv_bruteforce_fraction,
     pin_conv_sample_consistency,
+    pin_grad_torch, pin_grad_adjoint, pin_grad_1x1_is_gemm, pin_grad_golden, pin_grad_sample_consistency,
 ]
