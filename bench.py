@@ -136,7 +136,7 @@ def run_suite(reps, warmup):
             fn = igc.gemm_fp16 if c["dtype"] == "fp16" else igc.gemm_bf16
             la, lb = (igc.ROW_MAJOR if c[k] == "row" else igc.COL_MAJOR for k in ("la", "lb"))
             call = lambda: igc.check(fn(c["M"], c["N"], c["K"], dA, lda, la, dB, ldb, lb, dC, c["N"],
-                                        igc.OUT_CODES[c["out"]], stream))
+                                        igc.OUT_CODES[c["out"]], stream=stream))
             t = igc.igc_default_tune(c["M"], c["N"], c["K"])
         else:
             x, w = inputs.workload_operands(name)
@@ -144,10 +144,11 @@ def run_suite(reps, warmup):
             dx = torch.from_numpy(x.view(np.int16)).cuda()
             dw = torch.from_numpy(w.view(np.int16)).cuda()
             dy = torch.empty((c["N"] * P * Q * c["K"],), dtype=out_dt, device="cuda")
-            call = lambda: igc.check(igc.conv2d_nhwc_implicit_gemm_ex(
+            cfn = igc.conv2d_nhwc_implicit_gemm_fp16_ex if c["dtype"] == "fp16" else igc.conv2d_nhwc_implicit_gemm_ex
+            call = lambda: igc.check(cfn(
                 c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"], c["ph"], c["pw"], c["dh"],
-                c["dw"], dx, dw, dy, igc.OUT_CODES[c["out"]], 1 if c["dtype"] == "fp16" else 0, None, stream))
-            t = igc.igc_default_tune(c["N"] * P * Q, c["K"], c["R"] * c["S"] * c["C"], conv=1)
+                c["dw"], dx, dw, dy, igc.OUT_CODES[c["out"]], stream=stream))
+            t = igc.igc_default_tune(c["N"] * P * Q, c["K"], c["R"] * c["S"] * c["C"], op=igc.OP_CONV_FPROP)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -223,12 +224,12 @@ def main():
         if ev:
             ev[0].record(stream)
         igc.check(igc.gemm_bf16_ex(g["M"], g["N"], g["K"], dA, lda, igc.ROW_MAJOR, dB, ldb, igc.ROW_MAJOR, dC,
-                                   g["N"], igc.OUT_BF16, gtune, stream))
+                                   g["N"], igc.OUT_BF16, gtune, stream=stream))
         if ev:
             ev[1].record(stream)
         igc.check(igc.conv2d_nhwc_implicit_gemm_ex(c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"],
                                                    c["sw"], c["ph"], c["pw"], c["dh"], c["dw"], dx, dw, dy,
-                                                   igc.OUT_BF16, 0, ctune, stream))
+                                                   igc.OUT_BF16, ctune, stream=stream))
         if ev:
             ev[2].record(stream)
 
@@ -265,7 +266,8 @@ def main():
     total_ms = evs[0][0].elapsed_time(evs[-1][2])
     ms_per_step = total_ms / args.steps
     gf, cf = gemm_flops(g), conv_flops(c)
-    t_used = igc.igc_default_tune(g["M"], g["N"], g["K"]) if gtune is None else igc.Tune(*gtune)
+    t_used = igc.igc_default_tune(g["M"], g["N"], g["K"]) if gtune is None else igc.Tune(*gtune) if len(gtune) >= 10 \
+        else igc.tune(gtune)
     tune_str = ",".join(map(str, t_used.astuple()))
     value = (gf + cf) / (ms_per_step * 1e-3) / 1e12
     gemm_tflops = gf / (gemm_ms.mean() * 1e-3) / 1e12

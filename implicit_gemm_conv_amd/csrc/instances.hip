@@ -1,42 +1,66 @@
 // instances.hip -- instantiates the mainloop kernel for one tile configuration
-// (IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, IGC_LW given on the command line) with
-// every input type and operand layout: 8 GEMM kernels and 2 implicit-GEMM conv
-// kernels.
+// (IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, IGC_LW, IGC_SYNC
+// given on the command line) and one operation family IGC_FAMILY:
+//   0: bf16 GEMM (every operand layout; with IGC_FULL 0 only row-major A)
+//   1: fp16 GEMM (every operand layout; with IGC_FULL 0 only row-major A)
+//   2: forward convolution (bf16 and fp16; with IGC_FULL 0 bf16 only)
+//   3: data gradient (bf16 and fp16)
+//   4: filter gradient (bf16 and fp16)
+// and registers the table when the library is loaded.  With IGC_FULL 0 the
+// kernels carry only their main loop variant (K % 8 == 0 for the GEMM, whole
+// filter taps per K tile and filters of at most 16 x 16 for the convolution).
 #include "instances.hpp"
 #include "mainloop.hpp"
 
 #if !defined(IGC_BM) || !defined(IGC_BN) || !defined(IGC_BK) || !defined(IGC_D) || !defined(IGC_W) || \
-    !defined(IGC_MI) || !defined(IGC_HALF) || !defined(IGC_LW)
-#error "compile with -DIGC_BM=.. -DIGC_BN=.. -DIGC_BK=.. -DIGC_D=.. -DIGC_W=.. -DIGC_MI=.. -DIGC_HALF=.. -DIGC_LW=.."
+    !defined(IGC_MI) || !defined(IGC_HALF) || !defined(IGC_LW) || !defined(IGC_SYNC) || !defined(IGC_FULL) || \
+    !defined(IGC_FAMILY)
+#error "compile with -DIGC_BM=.. -DIGC_BN=.. -DIGC_BK=.. -DIGC_D=.. -DIGC_W=.. -DIGC_MI=.. -DIGC_HALF=.. -DIGC_LW=.. -DIGC_SYNC=.. -DIGC_FULL=.. -DIGC_FAMILY=.."
 #endif
-
-#define IGC_CAT9(a, b, c, d, e, f, g, h, i) a##b##x##c##x##d##x##e##x##f##x##g##x##h##x##i
-#define IGC_TABLE_NAME(BM, BN, BK, D, W, MI, H, L) IGC_CAT9(instance_table_, BM, BN, BK, D, W, MI, H, L)
 
 namespace igc {
 
-template <bool FP16, bool AKC, bool BKC, bool CONV>
-using Here = Cfg<FP16, IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, IGC_LW, AKC, BKC, CONV>;
+template <bool FP16, bool AKC, bool BKC, int OPK>
+using Here = Cfg<FP16, IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, IGC_LW, IGC_SYNC, AKC, BKC, OPK>;
 
-#define IGC_ENTRY(FP16, AKC, BKC, CONV)                                                                   \
-    Instance {                                                                                           \
-        IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, Here<FP16, AKC, BKC, CONV>::NL, FP16, AKC, BKC, \
-            CONV,                                                                                        \
-            reinterpret_cast<const void*>(&gemm_kernel<Here<FP16, AKC, BKC, CONV>>),                     \
-            Here<FP16, AKC, BKC, CONV>::LDS_BYTES                                                        \
+#define IGC_ENTRY(FP16, AKC, BKC, OPK)                                                                        \
+    Instance {                                                                                               \
+        IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, Here<FP16, AKC, BKC, OPK>::NL, IGC_SYNC, OPK, \
+            FP16, AKC, BKC, IGC_FULL != 0,                                                                  \
+            reinterpret_cast<const void*>(&gemm_kernel<Here<FP16, AKC, BKC, OPK>, IGC_FULL != 0>),           \
+            Here<FP16, AKC, BKC, OPK>::LDS_BYTES                                                             \
     }
 
 static const Instance kTable[] = {
-    IGC_ENTRY(false, true, true, false),  IGC_ENTRY(false, true, false, false),
-    IGC_ENTRY(false, false, true, false), IGC_ENTRY(false, false, false, false),
-    IGC_ENTRY(true, true, true, false),   IGC_ENTRY(true, true, false, false),
-    IGC_ENTRY(true, false, true, false),  IGC_ENTRY(true, false, false, false),
-    IGC_ENTRY(false, true, true, true),   IGC_ENTRY(true, true, true, true),
+#if IGC_FAMILY == 0
+    IGC_ENTRY(false, true, true, OP_GEMM), IGC_ENTRY(false, true, false, OP_GEMM),
+#if IGC_FULL
+    IGC_ENTRY(false, false, true, OP_GEMM), IGC_ENTRY(false, false, false, OP_GEMM),
+#endif
+#elif IGC_FAMILY == 1
+    IGC_ENTRY(true, true, true, OP_GEMM), IGC_ENTRY(true, true, false, OP_GEMM),
+#if IGC_FULL
+    IGC_ENTRY(true, false, true, OP_GEMM), IGC_ENTRY(true, false, false, OP_GEMM),
+#endif
+#elif IGC_FAMILY == 2
+    IGC_ENTRY(false, true, true, OP_FPROP),
+#if IGC_FULL
+    IGC_ENTRY(true, true, true, OP_FPROP),
+#endif
+#elif IGC_FAMILY == 3
+    IGC_ENTRY(false, true, false, OP_DGRAD), IGC_ENTRY(true, true, false, OP_DGRAD),
+#elif IGC_FAMILY == 4
+    IGC_ENTRY(false, false, false, OP_WGRAD), IGC_ENTRY(true, false, false, OP_WGRAD),
+#else
+#error "IGC_FAMILY must be 0..4"
+#endif
 };
 
-const Instance* IGC_TABLE_NAME(IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, IGC_LW)(int* count) {
-    *count = (int)(sizeof(kTable) / sizeof(kTable[0]));
-    return kTable;
-}
+namespace {
+struct Registrar {
+    Registrar() { register_instances(kTable, (int)(sizeof(kTable) / sizeof(kTable[0]))); }
+};
+const Registrar registrar;
+}  // namespace
 
 }  // namespace igc

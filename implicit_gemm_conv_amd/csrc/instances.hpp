@@ -8,21 +8,22 @@
 namespace igc {
 
 struct Instance {
-    int bm, bn, bk, d, waves, mfma, half, loaders;
-    bool fp16, a_kc, b_kc, conv;
-    const void* fn;      // __global__ gemm_kernel<Cfg<...>>
+    int bm, bn, bk, d, waves, mfma, half, loaders, sync;
+    int op;              // OpKind: 0 GEMM, 1 forward conv, 2 data gradient, 3 filter gradient
+    bool fp16, a_kc, b_kc;
+    bool full;           // every loop variant compiled (else only K % 8 == 0 GEMMs and whole-tap convolutions)
+    const void* fn;      // __global__ gemm_kernel<Cfg<...>, full>
     int64_t lds_bytes;   // static LDS of one workgroup
 };
 
-// One table per tile configuration, defined in instances.hip.
-#define IGC_DECLARE_TABLE(BM, BN, BK, D, W, MI, H, L) \
-    const Instance* instance_table_##BM##x##BN##x##BK##x##D##x##W##x##MI##x##H##x##L(int* count);
-IGC_FOR_EACH_TILE(IGC_DECLARE_TABLE)
-#undef IGC_DECLARE_TABLE
+// Each compiled object (one configuration, one operation family) registers
+// its table when the library is loaded.
+void register_instances(const Instance* table, int count);
 
-const Instance* find_instance(const igc_tune_t& t, bool fp16, bool a_kc, bool b_kc, bool conv);
-igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, bool conv);
+const Instance* find_instance(const igc_tune_t& t, bool fp16, bool a_kc, bool b_kc, int op);
+igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op);
 int num_tunes();
 igc_tune_t tune_at(int i);
+bool tune_is_full(int i);
 
 }  // namespace igc

@@ -79,10 +79,26 @@ constexpr int kRsrcFlags = 0x00020000;          // gfx9 raw buffer: 32-bit dword
 
 enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
+// What the mainloop computes.  Every operation is one GEMM C = A * B whose
+// operands are read in place; the convolutions differ only in how a tile's
+// rows and K indices map to addresses (the implicit-GEMM views):
+//   OP_GEMM : A (M x K) and B (K x N) dense, either layout.
+//   OP_FPROP: forward convolution.  Rows m = output pixels (n, p, q), K index
+//             = (filter tap, input channel); A gathers x (NHWC, channel
+//             contiguous), B = w as an N x K column-major matrix (KRSC).
+//   OP_DGRAD: data gradient.  Rows m = input pixels (n, h, w), K index =
+//             (filter tap, output channel); A gathers dy (NPQK) at the output
+//             pixel whose forward window puts that tap on (h, w), B row k*R*S
+//             + tap of w (KRSC) holds that tap's C input channels contiguously.
+//   OP_WGRAD: filter gradient.  Rows m = output channels, columns = (tap,
+//             input channel), K index = output pixels (n, p, q); A = dy read
+//             column-major (NPQK), B gathers x at each pixel's tap position.
+enum OpKind : int { OP_GEMM = 0, OP_FPROP = 1, OP_DGRAD = 2, OP_WGRAD = 3 };
+
 struct Params {
-    const void* A;   // GEMM A, or conv x (NHWC)
-    const void* B;   // GEMM B, or conv w (KRSC)
-    void* C;         // row-major M x N (conv: NPQK)
+    const void* A;   // GEMM A; conv: x (FPROP), dy (DGRAD, WGRAD)
+    const void* B;   // GEMM B; conv: w (FPROP, DGRAD), x (WGRAD)
+    void* C;         // row-major M x N (FPROP: y NPQK; DGRAD: dx NHWC; WGRAD: dw KRSC)
     int64_t M, N, K; // GEMM view
     int64_t lda, ldb, ldc;
     int tiles_m, tiles_n;
@@ -97,33 +113,49 @@ struct Params {
     int64_t ldws, ws_stride;
     int k_ragged8;   // K % 8 != 0: chunk straddling K must be zeroed
     int vec_ok;      // output rows allow 8/16-byte vector stores
-    // convolution geometry (CONV instances only)
-    int H, W, Cin, R, S, P, Q, sh, sw, ph, pw, dh, dw;
-    // stream-K (sk_grid > 0 workgroups): the tiles' K ranges, in units of the
-    // ring period (sk_units per tile), are cut into sk_grid equal runs; a
-    // workgroup whose run ends inside a tile publishes an fp32 partial tile in
-    // sk_ws (one BM x BN slot per workgroup) and raises its flag, the pair
-    // sk_flags[2*index .. 2*index+1] = (epoch, ~epoch);
-    // the workgroup that computes the tile's last K unit adds the partials of
-    // the lower workgroups in descending order and stores the tile.  Flags
-    // are raised to this call's epoch, so the workspace needs no clearing.
+    // convolution geometry: input N x H x W x Cin, filter R x S, output P x Q x Kc
+    int H, W, Cin, Kc, R, S, P, Q, sh, sw, ph, pw, dh, dw;
+    // The gathered operand of FPROP and DGRAD (A, channel contiguous): the
+    // image it reads (gH x gW pixels of gC channels), the pixel grid of the
+    // GEMM rows (rP x rQ), where row pixel (a, b) puts filter tap (0, 0)
+    // (a*rsh + roh, b*rsw + row) and how far one filter row / column moves in
+    // the image (tdh, tdw).  FPROP: x, rows over P x Q, (a*sh - ph, b*sw - pw),
+    // steps (dh, dw).  DGRAD: dy, rows over H x W, (a + ph, b + pw), steps
+    // (-dh, -dw), and a landing position is an image row/column only when it
+    // is a multiple of the stride (gsh, gsw; 1 for FPROP).
+    int gH, gW, gC, rP, rQ, rsh, rsw, roh, row, tdh, tdw, gsh, gsw;
+    uint32_t gsh_magic, gsw_magic;
+    // stream-K (sk_grid > 0 persistent workgroups).  Workgroup g first runs
+    // whole tiles g, g+G, ... below sk_dp_tiles (data-parallel rounds), then
+    // the K ranges of the remaining tiles, in units of the ring period
+    // (sk_units per tile), cut into sk_grid equal runs: a workgroup whose run
+    // ends inside a tile publishes an fp32 partial tile in sk_ws (one BM x BN
+    // slot per workgroup) and raises its flag sk_flags[g] to 1; the workgroup
+    // that computes the tile's last K unit adds the partials of the lower
+    // workgroups in descending order and stores the tile.  The flags are
+    // cleared by a kernel launched just before on the same stream.
     int sk_grid;
     int64_t sk_units;
+    int64_t sk_dp_tiles;
     float* sk_ws;
     int* sk_flags;
-    int sk_epoch;  // value a flag takes when raised in this call (31 bits, distinct from earlier calls)
-    int conv_uniform;  // Cin % BK == 0: every K tile lies within one filter tap
-    int conv_masks;    // R <= 16 and S <= 16: tap validity from per-row bit masks
-    int tpt;           // K tiles per filter tap (Cin / BK) when conv_uniform
-    uint32_t cin_magic, s_magic, tpt_magic;  // fastdiv multipliers for Cin, S and tpt
+    int sk_spin_limit;  // polls of a flag before the owner gives up
+    int sk_drop;        // test hook: the workgroup whose flag is never raised (-1: none)
+    int* err_word;      // set to 1 when a bounded wait gives up (the tile is then written as NaN)
+    int conv_uniform;  // gC % BK == 0: every K tile lies within one filter tap
+    int conv_masks;    // unit stride (DGRAD), R <= 16 and S <= 16: tap validity from per-row bit masks
+    int tpt;           // K tiles per filter tap (gC / BK) when conv_uniform
+    uint32_t cin_magic, s_magic, tpt_magic;  // fastdiv multipliers for gC, S and tpt
+    uint32_t q_magic, pq_magic;              // WGRAD pixel decode: Q and P*Q
 };
 
 // Loop variants, chosen per call and compiled as separate loops so that none
 // carries a branch between its MFMAs: GEMM with K % 8 == 0 or convolution
 // whose channel tiles straddle filter taps (PLAIN), K % 8 != 0 (RAGGED),
 // convolution with whole filter taps per K tile (UNIFORM_TAP), and convolution
-// with a filter wider or taller than 16 taps (CONV_GENERIC; the others keep a
-// per-row bit mask of the filter rows and columns that fall inside the image).
+// with a filter wider or taller than 16 taps or a strided data gradient
+// (CONV_GENERIC; the others keep a per-row bit mask of the filter rows and
+// columns that fall inside the image).  The filter gradient has one form.
 enum LoopVariant : int { PLAIN = 0, UNIFORM_TAP = 1, RAGGED = 2, CONV_GENERIC = 3 };
 
 // XOR swizzle of the 16-byte chunk index within a K-contiguous LDS row of CPR
@@ -215,8 +247,8 @@ struct Tile {
     }
 };
 
-template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, int MI_, int HALF_, int NL_, bool A_KC_,
-          bool B_KC_, bool CONV_>
+template <bool FP16_, int BM_, int BN_, int BK_, int D_, int NW_, int MI_, int HALF_, int NL_, int SYNC_, bool A_KC_,
+          bool B_KC_, int OPK_>
 struct Cfg {
     static constexpr bool FP16 = FP16_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_, D = D_;
@@ -245,7 +277,19 @@ struct Cfg {
     // refilled by loads interleaved through tile t's k-steps, instead of one
     // burst after the barrier.
     static constexpr bool SPREAD = Ring::spread(U);
-    static constexpr bool A_KC = A_KC_, B_KC = B_KC_, CONV = CONV_;
+    static constexpr bool A_KC = A_KC_, B_KC = B_KC_;
+    static constexpr int OPK = OPK_;
+    static constexpr bool FPROP = OPK == OP_FPROP, DGRAD = OPK == OP_DGRAD, WGRAD = OPK == OP_WGRAD;
+    // the operand gathered through an im2col map with per-row tap masks (A of FPROP and DGRAD)
+    static constexpr bool GATHER_A = FPROP || DGRAD;
+    static_assert(OPK == OP_GEMM || (FPROP && A_KC && B_KC) || (DGRAD && A_KC && !B_KC) || (WGRAD && !A_KC && !B_KC),
+                  "operand layouts of the convolution views");
+    // SYNC 0: one workgroup barrier per K tile is both "ready" and "free".
+    // SYNC 1: per-slot LDS counters -- loading waves count a slot ready once
+    // their loads into it have landed, every wave counts it free once its
+    // reads of it are done, and waves wait only on the counter they need.
+    static constexpr int SYNC = SYNC_;
+    static_assert(SYNC == 0 || SYNC == 1, "barrier ring or counter ring");
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave sub-tile is whole MFMA blocks");
@@ -264,7 +308,6 @@ struct Cfg {
     static constexpr int LPT = TA::IPW + TB::IPW;     // loads per K tile per wave
     // the slot pattern repeats every P tiles; the K loop is unrolled by P
     static constexpr int P = Ring::period(U);
-    static_assert(!CONV || A_KC, "im2col operand is channel (K) contiguous");
     static_assert(HALF == 0 || HALF == 1, "at most one extra operand slot");
     static_assert(HALF == 0 || D >= 2, "an odd ring needs at least five operand slots");
     // fragments alternate between two register sets by k-step, so one period
@@ -291,7 +334,8 @@ struct DmaState {
 template <class C, int V, bool LOADER = true>
 struct Mainloop {
     static constexpr bool kRagged = V == RAGGED, kUniformTap = V == UNIFORM_TAP;
-    static constexpr bool kConvMasks = C::CONV && V != CONV_GENERIC;
+    static constexpr bool kConvMasks = C::GATHER_A && V != CONV_GENERIC;
+    static constexpr bool kConvGeneric = C::GATHER_A && V == CONV_GENERIC;
     // LOADER: this wave issues global->LDS loads (waves 0 .. NL-1)
     using TA = typename C::TA;
     using TB = typename C::TB;
@@ -308,16 +352,24 @@ struct Mainloop {
     int KTp;         // KT rounded up to a multiple of the ring period (padding tiles load zeros)
     DmaState<TA::IPW> da;
     DmaState<TB::IPW> db;
-    // im2col: per A instruction, the pixel base offset and top-left input coordinate
+    // im2col (A of FPROP and DGRAD): per A instruction, the row pixel's gather state.
     // masked form: byte offset of the row's pixel at filter tap (0, 0) (may be
     // negative at the padding) and its tap mask (bit r: filter row r lands in
     // the image; bit 16+s: filter column s does; 0 for rows past M)
     int conv_base[kConvMasks ? TA::IPW : 1];
     uint32_t conv_mask[kConvMasks ? TA::IPW : 1];
-    // generic form: image base, top-left input row and column of the window
-    int conv_pix[C::CONV && !kConvMasks ? TA::IPW : 1];
-    int conv_h0[C::CONV && !kConvMasks ? TA::IPW : 1];
-    int conv_w0[C::CONV && !kConvMasks ? TA::IPW : 1];
+    // generic form: image base, top-left landing row and column of the window
+    int conv_pix[kConvGeneric ? TA::IPW : 1];
+    int conv_h0[kConvGeneric ? TA::IPW : 1];
+    int conv_w0[kConvGeneric ? TA::IPW : 1];
+    // DGRAD B, taps straddling K tiles: the byte offset of the lane's columns (or kOob)
+    uint32_t dg_col[C::DGRAD && !kUniformTap ? TB::IPW : 1];
+    // WGRAD B: per B instruction, the lane's column as a tap offset in the
+    // window (filter row r*dh, column s*dw; r*dh is huge for columns past N)
+    // and its channel byte offset
+    int wg_rd[C::WGRAD ? TB::IPW : 1];
+    int wg_sd[C::WGRAD ? TB::IPW : 1];
+    int wg_c2[C::WGRAD ? TB::IPW : 1];
     // the swizzled K chunk this lane fetches (same for all its loads of an operand)
     int ca_lane = 0, cb_lane = 0;
     // fragment read offsets (bytes within a stage's operand region)
@@ -348,23 +400,25 @@ struct Mainloop {
             const int q = j * C::NL + wave;
             const int row = TA::row_of(q, lane);
             const int c = TA::logical_chunk(q, lane);
-            if constexpr (C::CONV) {
+            if constexpr (C::GATHER_A) {
+                // row m = pixel (n, a, b) of the rP x rQ grid; filter tap (0, 0)
+                // lands on (h0, w0) of the gathered gH x gW image
                 const int64_t m = m0 + row;
-                const int PQ = p.P * p.Q;
+                const int PQ = p.rP * p.rQ;
                 const int mm = (int)(m < p.M ? m : 0);
                 const int n = mm / PQ, pq = mm - n * PQ;
-                const int pp = pq / p.Q, qq = pq - pp * p.Q;
-                const int h0 = pp * p.sh - p.ph, w0 = qq * p.sw - p.pw;
+                const int pa = pq / p.rQ, pb = pq - pa * p.rQ;
+                const int h0 = pa * p.rsh + p.roh, w0 = pb * p.rsw + p.row;
                 if constexpr (kConvMasks) {
                     uint32_t mask = 0;
                     for (int r = 0; r < p.R; ++r)
-                        if ((unsigned)(h0 + r * p.dh) < (unsigned)p.H) mask |= 1u << r;
+                        if ((unsigned)(h0 + r * p.tdh) < (unsigned)p.gH) mask |= 1u << r;
                     for (int s = 0; s < p.S; ++s)
-                        if ((unsigned)(w0 + s * p.dw) < (unsigned)p.W) mask |= 1u << (16 + s);
+                        if ((unsigned)(w0 + s * p.tdw) < (unsigned)p.gW) mask |= 1u << (16 + s);
                     conv_mask[j] = m < p.M ? mask : 0u;
-                    conv_base[j] = (((n * p.H + h0) * p.W + w0) * p.Cin) * 2;
+                    conv_base[j] = (((n * p.gH + h0) * p.gW + w0) * p.gC) * 2;
                 } else {
-                    conv_pix[j] = n * p.H * p.W * p.Cin;
+                    conv_pix[j] = n * p.gH * p.gW * p.gC;
                     conv_h0[j] = m < p.M ? h0 : -(1 << 28);  // invalid rows never hit the image
                     conv_w0[j] = w0;
                 }
@@ -393,6 +447,17 @@ struct Mainloop {
                 // B row-major (K x N storage): LDS row = k, chunk c covers n = n0 + 8c .. +7
                 const bool ok = n0 + 8 * c < p.N;
                 db.voff[j] = ok ? (uint32_t)(row * p.ldb * 2 + c * 16) : kOob;
+                if constexpr (C::DGRAD && !kUniformTap) dg_col[j] = ok ? (uint32_t)(c * 16) : kOob;
+                if constexpr (C::WGRAD) {
+                    // column n0 + 8c = (tap, channel) of the filter gradient; a
+                    // chunk never straddles taps since Cin % 8 == 0
+                    const int nc = (int)(ok ? n0 + 8 * c : 0);
+                    const int tap = nc / p.Cin, ch = nc - tap * p.Cin;
+                    const int r = tap / p.S, sc = tap - r * p.S;
+                    wg_rd[j] = ok ? r * p.dh : -(1 << 28);
+                    wg_sd[j] = sc * p.dw;
+                    wg_c2[j] = ch * 2;
+                }
             }
         }
     }
@@ -457,9 +522,9 @@ struct Mainloop {
         const int krem = krem64 <= 0 ? 0 : (krem64 >= BK ? BK : (int)krem64);
         // ---- A
         if constexpr (OP == 0 && J1 > J0) {
-            if constexpr (C::CONV) {
+            if constexpr (C::GATHER_A) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A);
-                // K index k = ((r*S + s) * Cin + c): filter tap (r, s), channel c.
+                // K index k = ((r*S + s) * gC + c): filter tap (r, s), channel c.
                 // This lane's chunk is the same logical chunk for all its loads.
                 int r, s, cin;
                 if constexpr (kUniformTap) {
@@ -472,17 +537,17 @@ struct Mainloop {
                     cin = (int)(tg - tap * (uint32_t)p.tpt) * BK + 8 * ca_lane;
                 } else {
                     const uint32_t kg = (uint32_t)k0 + 8u * (uint32_t)ca_lane;
-                    const uint32_t tap = fastdiv(kg, (uint32_t)p.Cin, p.cin_magic);
+                    const uint32_t tap = fastdiv(kg, (uint32_t)p.gC, p.cin_magic);
                     const uint32_t rr = fastdiv(tap, (uint32_t)p.S, p.s_magic);
                     r = (int)rr;
                     s = (int)(tap - rr * (uint32_t)p.S);
-                    cin = (int)(kg - tap * (uint32_t)p.Cin);
+                    cin = (int)(kg - tap * (uint32_t)p.gC);
                 }
                 const bool kok = 8 * ca_lane < krem;
                 if constexpr (kConvMasks) {
                     // tap (r, s) of a row is in the image iff both its mask bits are set
                     const uint32_t need = (1u << (r & 15)) | (1u << (16 + (s & 15)));
-                    const int toff = ((r * p.dh * p.W + s * p.dw) * p.Cin + cin) * 2;
+                    const int toff = ((r * p.tdh * p.gW + s * p.tdw) * p.gC + cin) * 2;
                     static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                         constexpr int j = J;
                         const int q = j * C::NL + wave;
@@ -490,14 +555,26 @@ struct Mainloop {
                         dma16(rs, sa + q * 1024, ok ? (uint32_t)(conv_base[j] + toff) : kOob);
                     });
                 } else {
-                    const int dhr = r * p.dh, dws = s * p.dw;
+                    const int dhr = r * p.tdh, dws = s * p.tdw;
                     static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                         constexpr int j = J;
                         const int q = j * C::NL + wave;
-                        const int h = conv_h0[j] + dhr;
-                        const int w = conv_w0[j] + dws;
-                        const bool ok = kok && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
-                        const uint32_t off = (uint32_t)(conv_pix[j] + (h * p.W + w) * p.Cin + cin) * 2u;
+                        int h = conv_h0[j] + dhr;
+                        int w = conv_w0[j] + dws;
+                        bool ok = kok;
+                        if constexpr (C::DGRAD) {
+                            // the tap lands on an output row/column only at multiples of the stride
+                            const int hq = (int)fastdiv((uint32_t)(h < 0 ? 0 : h), (uint32_t)p.gsh, p.gsh_magic);
+                            const int wq = (int)fastdiv((uint32_t)(w < 0 ? 0 : w), (uint32_t)p.gsw, p.gsw_magic);
+                            ok = ok && h >= 0 && w >= 0 && hq * p.gsh == h && wq * p.gsw == w;
+                            h = hq;
+                            w = wq;
+                        }
+                        ok = ok && (unsigned)h < (unsigned)p.gH && (unsigned)w < (unsigned)p.gW;
+                        // unsigned arithmetic: rows past M carry a huge negative h and are discarded
+                        const uint32_t off =
+                            ((uint32_t)conv_pix[j] + ((uint32_t)h * (uint32_t)p.gW + (uint32_t)w) * (uint32_t)p.gC +
+                             (uint32_t)cin) * 2u;
                         dma16(rs, sa + q * 1024, ok ? off : kOob);
                     });
                 }
@@ -526,6 +603,55 @@ struct Mainloop {
                 static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     dma16(rs, sb + (j * C::NL + wave) * 1024, kout ? kOob : db.voff[j]);
+                });
+            } else if constexpr (C::DGRAD) {
+                // K row k0 + i = (tap, output channel kc) reads filter row kc*R*S + tap
+                const int RS = p.R * p.S;
+                if constexpr (kUniformTap) {
+                    // the tile lies in one tap: rows kc0 .. kc0+BK-1 are ldb = R*S*Cin apart
+                    const uint32_t tap = fastdiv((uint32_t)k0, (uint32_t)p.gC, p.cin_magic);
+                    const int64_t kc0 = k0 - (int64_t)tap * p.gC;
+                    const __amdgpu_buffer_rsrc_t rs =
+                        make_rsrc((const char*)p.B + ((kc0 * RS + tap) * p.N + n0) * 2);
+                    static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = J;
+                        const int q = j * C::NL + wave;
+                        dma16(rs, sb + q * 1024, TB::row_of(q, lane) >= krem ? kOob : db.voff[j]);
+                    });
+                } else {
+                    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + n0 * 2);
+                    static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
+                        constexpr int j = J;
+                        const int q = j * C::NL + wave;
+                        const int row = TB::row_of(q, lane);
+                        const uint32_t kg = (uint32_t)k0 + (uint32_t)row;
+                        const uint32_t tap = fastdiv(kg, (uint32_t)p.gC, p.cin_magic);
+                        const uint32_t kc = kg - tap * (uint32_t)p.gC;
+                        const uint32_t off = (kc * (uint32_t)RS + tap) * (uint32_t)p.N * 2u + dg_col[j];
+                        dma16(rs, sb + q * 1024, (row >= krem || dg_col[j] == kOob) ? kOob : off);
+                    });
+                }
+            } else if constexpr (C::WGRAD) {
+                // K row k0 + i = output pixel (n, p, q); its window's tap (r, s)
+                // reads x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][channel]
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.B);
+                const uint32_t PQ = (uint32_t)(p.P * p.Q);
+                static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
+                    constexpr int j = J;
+                    const int q = j * C::NL + wave;
+                    const int row = TB::row_of(q, lane);
+                    const uint32_t pix = (uint32_t)k0 + (uint32_t)row;
+                    const uint32_t n = fastdiv(pix, PQ, p.pq_magic);
+                    const uint32_t pq = pix - n * PQ;
+                    const uint32_t pp = fastdiv(pq, (uint32_t)p.Q, p.q_magic);
+                    const int qq = (int)(pq - pp * (uint32_t)p.Q);
+                    const int h = (int)pp * p.sh - p.ph + wg_rd[j];
+                    const int w = qq * p.sw - p.pw + wg_sd[j];
+                    const bool ok = row < krem && (unsigned)h < (unsigned)p.H && (unsigned)w < (unsigned)p.W;
+                    const uint32_t off =
+                        ((n * (uint32_t)p.H + (uint32_t)h) * (uint32_t)p.W + (uint32_t)w) * (uint32_t)p.Cin * 2u +
+                        (uint32_t)wg_c2[j];
+                    dma16(rs, sb + q * 1024, ok ? off : kOob);
                 });
             } else {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (k0 * p.ldb + n0) * 2);
@@ -585,7 +711,7 @@ struct Mainloop {
                 *e = v;
             }
         };
-        if constexpr (C::A_KC && !C::CONV) {
+        if constexpr (C::A_KC && !C::GATHER_A) {
 #pragma unroll
             for (int j = 0; j < TA::IPW; ++j) {
                 const int q = j * C::NL + wave;
@@ -674,8 +800,9 @@ struct Mainloop {
     static constexpr int kCoherentVolatile = kCoherent | (1 << 31);
 
     // Writes the partial tile, waits until this wave's stores are complete,
-    // and (once every wave is there) raises the flag.
-    __device__ __forceinline__ void sk_publish(const Acc (&acc)[FM][FN], float* part, int* flag, int epoch) {
+    // and (once every wave is there) raises the flag to 1.  `raise` false is
+    // the test hook that leaves one flag down.
+    __device__ __forceinline__ void sk_publish(const Acc (&acc)[FM][FN], float* part, int* flag, bool raise) {
         typedef __attribute__((ext_vector_type(4))) int i32x4_t;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(part);
 #pragma unroll
@@ -690,26 +817,29 @@ struct Mainloop {
                 }
         wait_vmcnt<0>();
         __syncthreads();
-        if (threadIdx.x == 0) {
-            typedef __attribute__((ext_vector_type(2))) int i32x2_t;
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2_t{epoch, ~epoch}, make_rsrc(flag), 0, 0, kCoherent);
-        }
+        if (threadIdx.x == 0 && raise) __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(flag), 0, 0, kCoherent);
     }
 
-    // Waits for a lower workgroup's flag (bounded: every wave leaves the loop
-    // even if the flag never rises) and adds its partial tile.
-    __device__ __forceinline__ void sk_collect(Acc (&acc)[FM][FN], const float* part, int* flag, int epoch) {
-        typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+    // Waits (bounded: at most `spins` polls) for a lower workgroup's flag and,
+    // if it rose, adds its partial tile.  Thread 0 polls; its verdict reaches
+    // every wave through the first word of the drained ring (`bcast`), so all
+    // waves agree.  Returns false if the wait gave up.  Every wave must call
+    // it, after its K loop.
+    __device__ __forceinline__ bool sk_collect(Acc (&acc)[FM][FN], const float* part, int* flag, int spins,
+                                               IGC_LDS int* bcast) {
+        __syncthreads();  // every wave is done reading the ring (and an earlier verdict)
         if (threadIdx.x == 0) {
             const __amdgpu_buffer_rsrc_t rf = make_rsrc(flag);
-            typedef __attribute__((ext_vector_type(2))) int i32x2_t;
-            for (int spins = 0; spins < (1 << 24); ++spins) {
-                const i32x2_t f = __builtin_amdgcn_raw_buffer_load_b64(rf, 0, 0, kCoherentVolatile);
-                if (f[0] == epoch && f[1] == ~epoch) break;
-                __builtin_amdgcn_s_sleep(2);
+            int up = 0;
+            for (int n = 0; n < spins && !up; ++n) {
+                up = __builtin_amdgcn_raw_buffer_load_b32(rf, 0, 0, kCoherentVolatile) == 1;
+                if (!up) __builtin_amdgcn_s_sleep(2);
             }
+            *(volatile IGC_LDS int*)bcast = up;
         }
         __syncthreads();
+        const bool up = *(volatile IGC_LDS int*)bcast != 0;
+        if (!up) return false;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(part);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -725,6 +855,7 @@ struct Mainloop {
                     acc[i][j][4 * c + 2] += v[2];
                     acc[i][j][4 * c + 3] += v[3];
                 }
+        return true;
     }
 
     // ---- epilogue: accumulators -> C ---------------------------------------
@@ -1111,9 +1242,13 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
 }
 
 // Calls f(variant) with the loop variant this call needs, as a constant.
-template <class C, class F>
+// ALL = false compiles only the main variant (plain GEMM K, whole filter taps
+// per K tile); the host never sends such a kernel a call that needs another.
+template <class C, bool ALL, class F>
 __device__ __forceinline__ void with_variant(const Params p, F&& f) {
-    if constexpr (C::CONV) {
+    if constexpr (!ALL) {
+        f(std::integral_constant<int, C::GATHER_A ? UNIFORM_TAP : PLAIN>{});
+    } else if constexpr (C::GATHER_A) {
         // channels are a multiple of 8, so K never is ragged
         if (!p.conv_masks)
             f(std::integral_constant<int, CONV_GENERIC>{});
@@ -1121,6 +1256,9 @@ __device__ __forceinline__ void with_variant(const Params p, F&& f) {
             f(std::integral_constant<int, UNIFORM_TAP>{});
         else
             f(std::integral_constant<int, PLAIN>{});
+    } else if constexpr (C::WGRAD) {
+        // neither operand is K-contiguous: a K tail is masked by whole LDS rows
+        f(std::integral_constant<int, PLAIN>{});
     } else {
         if (p.k_ragged8)
             f(std::integral_constant<int, RAGGED>{});
@@ -1132,21 +1270,75 @@ __device__ __forceinline__ void with_variant(const Params p, F&& f) {
 // End (exclusive) of stream-K workgroup g's run of K units.
 __device__ __forceinline__ int64_t sk_end(int64_t total, int G, int g) { return total * (g + 1) / G; }
 
-// Stream-K: workgroup g takes the K units [b, e) of the tiles' concatenated K
-// ranges and walks them backwards, one tile segment at a time, so that it
-// first finishes the segment it shares with higher workgroups (publishing a
-// partial) and last the segment whose tile it owns (collecting the partials of
-// lower workgroups, which published theirs first).  An owner therefore only
-// waits on workgroups dispatched no later than itself.
-template <class C>
-__device__ __forceinline__ void stream_k(const Params p) {
-    constexpr int UNIT = C::P * C::BK;  // K elements per unit (one ring period)
-    const int G = p.sk_grid, g = (int)blockIdx.x;
-    const int64_t UT = p.sk_units;
-    const int64_t total = (int64_t)p.tiles_m * p.tiles_n * UT;
-    const int64_t b = total * g / G;
-    int64_t hi = sk_end(total, G, g);
-    while (hi > b) {
+// One piece of work for a workgroup: the K range [kbase, kend) of output tile
+// (tm, tn), and what to do with the accumulators afterwards.
+enum Role : int {
+    ROLE_STORE = 0,    // the whole K range: store the tile to C
+    ROLE_SPLIT = 1,    // one split of a K split: store the fp32 partial tile to the workspace
+    ROLE_PUBLISH = 2,  // a stream-K segment below the tile's last K unit: publish the partial
+    ROLE_OWN = 3       // the stream-K segment with the tile's last K unit: collect, then store to C
+};
+struct WorkItem {
+    int tm, tn, role, split;
+    int64_t kbase, kend;
+    int64_t tile_start;  // ROLE_OWN: the tile's first K unit in the concatenated stream-K range
+};
+
+// The workgroup's schedule, one item at a time.
+//  * Data-parallel grid (sk_grid == 0): one item, tile blockIdx % T (in the
+//    XCD-aware order of tile_coords), K split blockIdx / T.
+//  * Stream-K (sk_grid = G): workgroup g first computes whole tiles g, g+G,
+//    ... below sk_dp_tiles (data-parallel rounds in the same XCD order), then
+//    takes the K units [b, e) of the remaining tiles' concatenated K ranges and
+//    walks them backwards, one tile segment at a time, so that it first
+//    finishes the segment it shares with higher workgroups (publishing a
+//    partial) and last the segment whose tile it owns (collecting the partials
+//    of lower workgroups, which published theirs first).  An owner therefore
+//    only waits on workgroups dispatched no later than itself.
+struct Schedule {
+    int G, g;
+    int64_t T, Tdp, UT, total, b, hi, blk;
+    bool done;
+
+    __device__ __forceinline__ explicit Schedule(const Params& p) {
+        G = p.sk_grid;
+        g = (int)blockIdx.x;
+        T = (int64_t)p.tiles_m * p.tiles_n;
+        done = false;
+        if (G > 0) {
+            Tdp = p.sk_dp_tiles;
+            UT = p.sk_units;
+            total = (T - Tdp) * UT;
+            b = total * g / G;
+            hi = sk_end(total, G, g);
+            blk = g;
+        }
+    }
+
+    template <int UNIT>
+    __device__ __forceinline__ bool next(const Params& p, WorkItem& it) {
+        if (G <= 0) {
+            if (done) return false;
+            done = true;
+            it.split = (int)(blockIdx.x / T);
+            tile_coords((int)(blockIdx.x - (int64_t)it.split * T), p.tiles_m, p.tiles_n, p.group_m, it.tm, it.tn);
+            it.kbase = (int64_t)it.split * p.k_per_split;
+            it.kend = it.kbase + p.k_per_split < p.K ? it.kbase + p.k_per_split : p.K;
+            it.role = p.k_splits > 1 ? ROLE_SPLIT : ROLE_STORE;
+            it.tile_start = 0;
+            return true;
+        }
+        if (blk < Tdp) {
+            tile_coords((int)blk, p.tiles_m, p.tiles_n, p.group_m, it.tm, it.tn);
+            it.kbase = 0;
+            it.kend = p.K;
+            it.role = ROLE_STORE;
+            it.split = 0;
+            it.tile_start = 0;
+            blk += G;
+            return true;
+        }
+        if (hi <= b) return false;
         const int64_t tau = (hi - 1) / UT;
         const int64_t lo = b > tau * UT ? b : tau * UT;
         const int64_t u0 = lo - tau * UT, u1 = hi - tau * UT;
@@ -1154,56 +1346,73 @@ __device__ __forceinline__ void stream_k(const Params p) {
         // run is processed at the same time: give it the tile the
         // data-parallel grid runs in round j on the same XCD, keeping that
         // grid's L2 grouping.
-        const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
+        const int64_t Tsk = T - Tdp;
         int64_t block = tau;
-        if (T % G == 0 && (total / G) % UT == 0) {
-            const int64_t c = T / G;
+        if (Tsk % G == 0 && (total / G) % UT == 0) {
+            const int64_t c = Tsk / G;
             block = (tau % c) * G + tau / c;
         }
-        int tm, tn;
-        tile_coords((int)block, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-        const int64_t kbase = u0 * UNIT;
-        const int64_t kend = u1 * UNIT < p.K ? u1 * UNIT : p.K;
-        with_variant<C>(p, [&](auto v) __attribute__((always_inline)) {
-            run_tile<C, decltype(v)::value>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
-                if (u1 < UT) {
-                    ml.sk_publish(acc, p.sk_ws + (int64_t)g * (C::BM * C::BN), p.sk_flags + 2 * g, p.sk_epoch);
-                } else {
-                    // owner: add the partials of the lower workgroups sharing this tile
-                    const int64_t tile_start = tau * UT;
-                    for (int gp = g - 1; gp >= 0 && sk_end(total, G, gp) > tile_start; --gp)
-                        ml.sk_collect(acc, p.sk_ws + (int64_t)gp * (C::BM * C::BN), p.sk_flags + 2 * gp,
-                                      p.sk_epoch);
-                    store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
-                }
-            });
-        });
+        tile_coords((int)(Tdp + block), p.tiles_m, p.tiles_n, p.group_m, it.tm, it.tn);
+        it.kbase = u0 * UNIT;
+        it.kend = u1 * UNIT < p.K ? u1 * UNIT : p.K;
+        it.role = u1 < UT ? ROLE_PUBLISH : ROLE_OWN;
+        it.split = 0;
+        it.tile_start = tau * UT;
         hi = lo;
-        __syncthreads();  // every wave is past this segment's LDS before the next prologue
+        return true;
+    }
+};
+
+// After the K loop of one work item.  Every wave calls it.
+template <class C, class ML>
+__device__ __forceinline__ void finish_item(ML& ml, typename C::Acc (&acc)[C::FM][C::FN], const Params& p,
+                                            const WorkItem& it, const Schedule& sch) {
+    if (it.role == ROLE_STORE) {
+        store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+    } else if (it.role == ROLE_SPLIT) {
+        ml.store(acc, p.ws + it.split * p.ws_stride, p.ldws, OUT_F32, true);
+    } else if (it.role == ROLE_PUBLISH) {
+        ml.sk_publish(acc, p.sk_ws + (int64_t)sch.g * (C::BM * C::BN), p.sk_flags + sch.g, sch.g != p.sk_drop);
+    } else {
+        // owner: add the partials of the lower workgroups sharing this tile, in
+        // descending order; the wait for each is bounded, and a partial that
+        // never arrives marks the tile (NaN) and the error word instead of
+        // leaving a silently wrong result
+        bool ok = true;
+        for (int gp = sch.g - 1; gp >= 0 && sk_end(sch.total, sch.G, gp) > it.tile_start; --gp)
+            ok = ml.sk_collect(acc, p.sk_ws + (int64_t)gp * (C::BM * C::BN), p.sk_flags + gp, p.sk_spin_limit,
+                               (IGC_LDS int*)slot<C, 0>()) && ok;
+        if (!ok) {
+            constexpr int NE = (int)(sizeof(typename C::Acc) / sizeof(float));
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) acc[i][j][e] = __builtin_nanf("");
+            if (threadIdx.x == 0) __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(p.err_word), 0, 0, 1 | 16);
+        }
+        store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
     }
 }
 
-template <class C>
+// The kernel: the workgroup's work items one after another.  The K loop is
+// instantiated once per loop variant (and per loading / compute-only wave),
+// whatever the schedule.
+template <class C, bool ALL>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
-    if (p.sk_grid > 0) {
-        stream_k<C>(p);
-        return;
-    }
-    // workgroups s*T .. s*T+T-1 (T output tiles) take K split s
-    const int T = p.tiles_m * p.tiles_n;
-    const int split = (int)blockIdx.x / T;
-    int tm, tn;
-    tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int64_t kbase = (int64_t)split * p.k_per_split;
-    const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
-    with_variant<C>(p, [&](auto v) __attribute__((always_inline)) {
-        run_tile<C, decltype(v)::value>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
-            if (p.k_splits > 1)
-                ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
-            else
-                store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+    constexpr int UNIT = C::P * C::BK;  // stream-K unit: K elements of one ring period
+    Schedule sch(p);
+    WorkItem it;
+    while (sch.template next<UNIT>(p, it)) {
+        with_variant<C, ALL>(p, [&](auto v) __attribute__((always_inline)) {
+            run_tile<C, decltype(v)::value>(p, it.tm, it.tn, it.kbase, it.kend,
+                                            [&](auto& ml, auto& acc) __attribute__((always_inline)) {
+                                                finish_item<C>(ml, acc, p, it, sch);
+                                            });
         });
-    });
+        __syncthreads();  // every wave is past this item's LDS before the next prologue
+    }
 }
 
 }  // namespace igc

@@ -7,7 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "igc.h"
+#include "igc_probes.h"
 #include "mainloop.hpp"
 
 namespace igc {

@@ -1,6 +1,7 @@
 // split_reduce.hip -- second pass of split-K: C = sum over splits of the fp32
 // partial tiles, added in split order 0, 1, ..., S-1 (fixed, so results are
-// bit-reproducible), then rounded once to the output type.
+// bit-reproducible), then rounded once to the output type.  Also the small
+// kernel that clears the stream-K flags before a stream-K launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +43,21 @@ hipError_t launch_split_reduce(const float* ws, int S, int64_t ws_stride, int64_
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ws, S, ws_stride, M, N,
                        ldws, C, ldc, kind);
+    return hipGetLastError();
+}
+
+// Zeroes n stream-K flags.  System-coherent stores (SC0 | SC1) write through
+// to memory, so the next kernel's flag polls on any XCD see the zero.
+__global__ __launch_bounds__(256) void sk_clear_flags_kernel(int* flags, int n) {
+    const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (i < n)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            0, __builtin_amdgcn_make_buffer_rsrc(flags, (short)0, 0x7fffffff, 0x00020000), i * 4, 0, 1 | 16);
+}
+
+hipError_t launch_clear_flags(int* flags, int n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sk_clear_flags_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, flags, n);
     return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-"""Ceilings of the hot path, measured with the library's probe kernels (include/igc.h, csrc/probes.hip).
+"""Ceilings of the hot path, measured with the probe kernels of libigc_probes.so (include/igc_probes.h,
+csrc/probes.hip), a library of their own beside libigc.so.
 
 * mfma_ceiling: TFLOP/s of an MFMA-only stream with the GEMM's wave tile on random register operands, and the
   shader clock it runs at (read in-kernel).  The GEMM's fraction of this is the per-clock efficiency left to win;
@@ -8,9 +9,42 @@
 
   python -m implicit_gemm_conv_amd.probes
 """
+import ctypes
+import os
+
 import numpy as np
 
 import implicit_gemm_conv_amd as igc
+
+PROBES_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libigc_probes.so")
+_plib = None
+
+
+def plib():
+    """The loaded libigc_probes.so; raises if it has not been built."""
+    global _plib
+    if _plib is None:
+        if not os.path.exists(PROBES_PATH):
+            raise RuntimeError(f"{PROBES_PATH} is missing: build it with `python -m implicit_gemm_conv_amd.build`")
+        igc.lib()  # the same HIP runtime as torch's (see implicit_gemm_conv_amd.lib)
+        L = ctypes.CDLL(PROBES_PATH)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.igc_probe_mfma.argtypes = [i32, i32, i32, i32, p, i64, p, i64, p]
+        L.igc_probe_mfma.restype = i32
+        L.igc_probe_dma.argtypes = [i32, i32, p, p, i64, p, i64, p]
+        L.igc_probe_dma.restype = i32
+        _plib = L
+    return _plib
+
+
+def igc_probe_mfma(mfma, waves, iters, grid, sink, sink_bytes, clk, clk_bytes, stream=None):
+    return plib().igc_probe_mfma(mfma, waves, iters, grid, igc._ptr(sink), sink_bytes, igc._ptr(clk), clk_bytes,
+                                 igc._stream(stream))
+
+
+def igc_probe_dma(bk, operands, A, B, bytes_each, clk, clk_bytes, stream=None):
+    return plib().igc_probe_dma(bk, operands, igc._ptr(A), igc._ptr(B), bytes_each, igc._ptr(clk), clk_bytes,
+                                igc._stream(stream))
 
 SPEC_CLOCK_GHZ = 2.4
 PEAK_BF16_TFLOPS = 2516.6
@@ -35,7 +69,7 @@ def mfma_ceiling(mfma=16, waves=8, iters=3000, grid=512, reps=3):
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        igc.check(igc.igc_probe_mfma(mfma, waves, iters, grid, sink, sink.numel() * 4, clk, clk.numel() * 4))
+        igc.check(igc_probe_mfma(mfma, waves, iters, grid, sink, sink.numel() * 4, clk, clk.numel() * 4))
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
@@ -60,7 +94,7 @@ def dma_throughput(bk, operands, reps=3):
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        igc.check(igc.igc_probe_dma(bk, operands, A, B, n * 2, clk, clk.numel() * 4))
+        igc.check(igc_probe_dma(bk, operands, A, B, n * 2, clk, clk.numel() * 4))
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)

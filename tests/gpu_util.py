@@ -38,18 +38,31 @@ def host_values(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def run_gemm(M, N, K, A, lda, la, B, ldb, lb, out="f32", dtype="bf16", ldc=None, tune=None, C=None):
+def run_gemm(M, N, K, A, lda, la, B, ldb, lb, out="f32", dtype="bf16", ldc=None, tune=None, C=None, workspace=None):
     """Runs the library GEMM on device copies of the bit arrays; returns (C[M,N] float64, raw buffer)."""
     ldc = ldc if ldc is not None else (N + 7) // 8 * 8 if out != "f32" else (N + 3) // 4 * 4
     dA, dB = to_dev(A), to_dev(B)
     buf = poisoned(M, ldc, out) if C is None else C
     fn = igc.gemm_fp16_ex if dtype == "fp16" else igc.gemm_bf16_ex
-    st = fn(M, N, K, dA, lda, LAYOUT[la], dB, ldb, LAYOUT[lb], buf, ldc, igc.OUT_CODES[out], tune)
+    st = fn(M, N, K, dA, lda, LAYOUT[la], dB, ldb, LAYOUT[lb], buf, ldc, igc.OUT_CODES[out], tune, workspace)
     igc.check(st)
-    torch.cuda.synchronize()
+    synchronize()
     full = host_values(buf)
     check_guards(full, M, N, ldc)
     return full[: M * ldc].reshape(M, ldc)[:, :N], buf
+
+
+def synchronize(seconds=60.0):
+    """Waits for the current stream with a deadline: a kernel that never finishes fails the test (with the stream
+    still busy) instead of blocking the run until the harness kills it."""
+    import time
+    stream = torch.cuda.current_stream()
+    t0 = time.monotonic()
+    while not stream.query():
+        if time.monotonic() - t0 > seconds:
+            raise TimeoutError(f"GPU work still running after {seconds} s")
+        time.sleep(0.0005)
+    torch.cuda.synchronize()
 
 
 def check_guards(full, M, N, ldc):
@@ -72,18 +85,31 @@ def assert_close(y, ref, S, out, what=""):
     return ratio
 
 
-def run_conv(N, H, W, C, K, R, S, x, w, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, out="f32", dtype="bf16", tune=None):
+CONV_FNS = {
+    ("fprop", "bf16"): igc.conv2d_nhwc_implicit_gemm_ex, ("fprop", "fp16"): igc.conv2d_nhwc_implicit_gemm_fp16_ex,
+    ("dgrad", "bf16"): igc.conv2d_nhwc_dgrad_implicit_gemm_ex,
+    ("dgrad", "fp16"): igc.conv2d_nhwc_dgrad_implicit_gemm_fp16_ex,
+    ("wgrad", "bf16"): igc.conv2d_nhwc_wgrad_implicit_gemm_ex,
+    ("wgrad", "fp16"): igc.conv2d_nhwc_wgrad_implicit_gemm_fp16_ex,
+}
+
+
+def run_conv(N, H, W, C, K, R, S, in0, in1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, out="f32", dtype="bf16", tune=None,
+             op="fprop", workspace=None):
+    """Runs one convolution operation through the C ABI.  fprop: (x, w) -> y [N, P, Q, K]; dgrad: (dy, w) -> dx
+    [N, H, W, C]; wgrad: (x, dy) -> dw [K, R, S, C]."""
     P, Q = oracle.conv_out_hw(H, W, R, S, sh, sw, ph, pw, dh, dw)
-    dx, dwt = to_dev(x), to_dev(w)
-    M = N * P * Q
-    buf = poisoned(M, K, out)
-    st = igc.conv2d_nhwc_implicit_gemm_ex(N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, dx, dwt, buf,
-                                          igc.OUT_CODES[out], 1 if dtype == "fp16" else 0, tune)
+    shape = {"fprop": (N, P, Q, K), "dgrad": (N, H, W, C), "wgrad": (K, R, S, C)}[op]
+    rows, ld = int(np.prod(shape[:-1])), shape[-1]
+    d0, d1 = to_dev(in0), to_dev(in1)
+    buf = poisoned(rows, ld, out)
+    st = CONV_FNS[(op, dtype)](N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw, d0, d1, buf, igc.OUT_CODES[out], tune,
+                               workspace)
     igc.check(st)
-    torch.cuda.synchronize()
+    synchronize()
     full = host_values(buf)
-    check_guards(full, M, K, K)
-    return full[: M * K].reshape(N, P, Q, K), buf
+    check_guards(full, rows, ld, ld)
+    return full[: rows * ld].reshape(shape), buf
 
 
 def round_to(values, out):

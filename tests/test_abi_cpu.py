@@ -17,22 +17,37 @@ HEADER = os.path.join(ROOT, "include", "igc.h")
 pytestmark = pytest.mark.skipif(not os.path.exists(igc.LIB_PATH), reason="libigc.so not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+PROBES_HEADER = os.path.join(ROOT, "include", "igc_probes.h")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
 
 
 def test_header_names():
     names = declared_functions()
-    for must in ("gemm_bf16", "gemm_fp16", "conv2d_nhwc_implicit_gemm", "igc_status_string", "igc_ring_schedule"):
+    for must in ("gemm_bf16", "gemm_fp16", "conv2d_nhwc_implicit_gemm", "conv2d_nhwc_implicit_gemm_fp16_ex",
+                 "conv2d_nhwc_dgrad_implicit_gemm", "conv2d_nhwc_wgrad_implicit_gemm", "igc_workspace_bytes",
+                 "igc_status_string", "igc_ring_schedule", "igc_take_device_error"):
         assert must in names
+    assert sorted(igc.EXPORTS) == names, "the binding's export list and the header disagree"
+    assert not any(n.startswith("igc_probe") for n in names), "probes live in their own library"
 
 
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(igc.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(L, n)]
     assert not missing, missing
+
+
+def test_probe_library_exports_every_declared_symbol():
+    from implicit_gemm_conv_amd import probes
+    L = ctypes.CDLL(probes.PROBES_PATH)
+    names = declared_functions(PROBES_HEADER)
+    assert names == ["igc_probe_dma", "igc_probe_mfma"]
+    assert all(hasattr(L, n) for n in names)
 
 
 def test_status_strings():
@@ -59,17 +74,24 @@ FAKE = 1 << 20  # a 16-byte aligned address that is never dereferenced (validati
     (dict(K=60, lda=60), igc.IGC_ERR_MISALIGNED),       # 60 * 2 bytes is not a multiple of 16
     (dict(ldc=66, c_type=igc.OUT_BF16), igc.IGC_ERR_MISALIGNED),
     (dict(tune=(64, 64, 64, 9, 4)), igc.IGC_ERR_UNSUPPORTED),
-    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 0, 2, 256)), igc.IGC_ERR_INVALID_VALUE),  # split-K and stream-K together
-    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, -1)), igc.IGC_ERR_INVALID_VALUE),
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 4, 2, 256)), igc.IGC_ERR_INVALID_VALUE),  # split-K and stream-K together
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 4, 1, -1)), igc.IGC_ERR_INVALID_VALUE),
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 4, 1, 0, 0, 1)), igc.IGC_ERR_INVALID_VALUE),  # hybrid without stream-K
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 4, 1, 256), ws=FAKE, ws_bytes=4096), igc.IGC_ERR_INVALID_VALUE),  # short
+    (dict(tune=(256, 256, 32, 4, 8, 16, 0, 4, 1, 256), ws=FAKE + 16, ws_bytes=1 << 30),
+     igc.IGC_ERR_INVALID_VALUE),                                                    # workspace not 256-byte aligned
+    (dict(K=40, lda=40, tune=(256, 256, 32, 2, 8, 32, 0, 4)), igc.IGC_ERR_UNSUPPORTED),  # study tile: no ragged K
     (dict(M=0), igc.IGC_OK),                            # empty output: no-op
     (dict(N=0), igc.IGC_OK),
 ])
 def test_gemm_validation(args, expect):
     a = dict(M=64, N=64, K=64, A=FAKE, lda=64, la=igc.ROW_MAJOR, B=FAKE, ldb=64, lb=igc.ROW_MAJOR, C=FAKE,
-             ldc=64, c_type=igc.OUT_F32, tune=None)
+             ldc=64, c_type=igc.OUT_F32, tune=None, ws=None, ws_bytes=0)
     a.update(args)
+    if a["K"] == 40:
+        a["K"] = 36  # ragged (36 % 8 != 0) with a valid 16-byte pitch
     st = igc.gemm_bf16_ex(a["M"], a["N"], a["K"], a["A"], a["lda"], a["la"], a["B"], a["ldb"], a["lb"], a["C"],
-                          a["ldc"], a["c_type"], a["tune"], stream=0)
+                          a["ldc"], a["c_type"], a["tune"], a["ws"], a["ws_bytes"], stream=0)
     assert st == expect, igc.igc_status_string(st)
 
 
@@ -86,15 +108,43 @@ def test_gemm_validation(args, expect):
     (dict(N=0), igc.IGC_OK),
     (dict(K=0), igc.IGC_OK),
     (dict(N=1 << 14, H=512, W=512), igc.IGC_ERR_UNSUPPORTED),  # x spans >= 2^31 bytes
+    # a 1x1 filter with huge padding: N*P*Q = 4 * 32001^2 >= 2^31 output rows
+    (dict(N=4, H=1, W=1, C=8, K=8, R=1, S=1, ph=16000, pw=16000), igc.IGC_ERR_UNSUPPORTED),
 ])
-def test_conv_validation(args, expect):
+@pytest.mark.parametrize("op", ["fprop", "dgrad", "wgrad"])
+def test_conv_validation(args, expect, op):
     a = dict(N=2, H=8, W=8, C=16, K=16, R=3, S=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, x=FAKE, w=FAKE, y=FAKE,
              y_type=igc.OUT_F32)
     a.update(args)
-    st = igc.conv2d_nhwc_implicit_gemm_ex(a["N"], a["H"], a["W"], a["C"], a["K"], a["R"], a["S"], a["sh"], a["sw"],
-                                          a["ph"], a["pw"], a["dh"], a["dw"], a["x"], a["w"], a["y"], a["y_type"],
-                                          0, None, stream=0)
+    fn = {"fprop": igc.conv2d_nhwc_implicit_gemm_ex, "dgrad": igc.conv2d_nhwc_dgrad_implicit_gemm_ex,
+          "wgrad": igc.conv2d_nhwc_wgrad_implicit_gemm_ex}[op]
+    if op != "fprop" and args.get("w") == FAKE + 4:
+        pytest.skip("same argument order check as the forward pass")
+    st = fn(a["N"], a["H"], a["W"], a["C"], a["K"], a["R"], a["S"], a["sh"], a["sw"], a["ph"], a["pw"], a["dh"],
+            a["dw"], a["x"], a["w"], a["y"], a["y_type"], None, None, 0, stream=0)
+    if (op, args.get("K"), args.get("N")) in (("dgrad", 0, None), ("wgrad", None, 0)):
+        # an empty sum: the output is written as zeros, which takes a launch (a GPU test covers it)
+        expect = igc.IGC_ERR_HIP if not _have_gpu() else igc.IGC_OK
     assert st == expect, igc.igc_status_string(st)
+
+
+def _have_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.parametrize("fn", [igc.conv2d_nhwc_dgrad_implicit_gemm, igc.conv2d_nhwc_wgrad_implicit_gemm,
+                                igc.conv2d_nhwc_dgrad_implicit_gemm_fp16, igc.conv2d_nhwc_wgrad_implicit_gemm_fp16])
+def test_gradient_channels_must_be_multiples_of_8(fn):
+    """The gradients read dy rows of K channels in 16-byte chunks: K % 8 != 0 is misaligned (the forward pass
+    accepts it)."""
+    st = fn(2, 8, 8, 16, 12, 3, 3, 1, 1, 1, 1, 1, 1, FAKE, FAKE, FAKE, igc.OUT_F32, stream=0)
+    assert st == igc.IGC_ERR_MISALIGNED
+    st = igc.conv2d_nhwc_implicit_gemm(2, 8, 8, 16, 12, 3, 3, 1, 1, 1, 1, 1, 1, 0, FAKE, FAKE, igc.OUT_F32, stream=0)
+    assert st == igc.IGC_ERR_INVALID_VALUE  # (x NULL: the forward pass got as far as the pointer check)
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -108,11 +158,12 @@ def test_conv_validation(args, expect):
     (dict(sink=FAKE + 2), igc.IGC_ERR_MISALIGNED),
 ])
 def test_probe_mfma_validation(args, expect):
+    from implicit_gemm_conv_amd import probes
     a = dict(mfma=16, waves=8, iters=10, grid=512, sink=FAKE, sink_bytes=512 * 8 * 64 * 4, clk=FAKE,
              clk_bytes=512 * 8)
     a.update(args)
-    st = igc.igc_probe_mfma(a["mfma"], a["waves"], a["iters"], a["grid"], a["sink"], a["sink_bytes"], a["clk"],
-                            a["clk_bytes"], stream=0)
+    st = probes.igc_probe_mfma(a["mfma"], a["waves"], a["iters"], a["grid"], a["sink"], a["sink_bytes"], a["clk"],
+                               a["clk_bytes"], stream=0)
     assert st == expect, igc.igc_status_string(st)
 
 
@@ -125,50 +176,80 @@ def test_probe_mfma_validation(args, expect):
     (dict(A=FAKE + 8), igc.IGC_ERR_MISALIGNED),
 ])
 def test_probe_dma_validation(args, expect):
+    from implicit_gemm_conv_amd import probes
     a = dict(bk=32, operands=3, A=FAKE, B=FAKE, bytes_each=8192 * 8192 * 2, clk=FAKE, clk_bytes=1024 * 8)
     a.update(args)
-    st = igc.igc_probe_dma(a["bk"], a["operands"], a["A"], a["B"], a["bytes_each"], a["clk"], a["clk_bytes"],
-                           stream=0)
+    st = probes.igc_probe_dma(a["bk"], a["operands"], a["A"], a["B"], a["bytes_each"], a["clk"], a["clk_bytes"],
+                              stream=0)
     assert st == expect, igc.igc_status_string(st)
 
 
 def test_tune_table_fits_lds():
     """Every compiled ring fits the 160 KB of LDS of one CU (a stage costs (BM+BN)*BK*2 bytes)."""
     tunes = igc.tunes()
-    assert (256, 256, 64, 2, 4, 32, 0, 4) in tunes and (256, 256, 32, 5, 8, 32, 0, 8) in tunes
-    assert (256, 256, 32, 4, 8, 16, 0, 8) in tunes and (256, 256, 64, 2, 8, 16, 1, 4) in tunes
-    for (bm, bn, bk, d, w, mi, h, lw) in tunes:
+    assert (256, 256, 32, 4, 8, 16, 0, 4, 0) in tunes and (256, 256, 64, 2, 8, 16, 1, 4, 0) in tunes
+    assert set(igc.tunes(full_only=True)) >= {(256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)}
+    for (bm, bn, bk, d, w, mi, h, lw, sy) in tunes:
         assert 1 <= lw <= w and w % lw == 0
-        lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw))
+        lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw, sy))
         U = 2 * d + h
         assert lds == ((bm + bn) * bk * 2 * d if U % 2 == 0 else U * max(bm, bn) * bk * 2)
         assert lds <= 160 * 1024
-        assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, lw)) == 1
+        assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, lw, sy)) == 1
         if lw == w:  # loader_waves 0 means every wave
-            assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, 0)) == 1
+            assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, 0, sy)) == 1
     assert igc.igc_tune_supported((256, 256, 64, 3, 4)) == 0  # 192 KB: over budget, not compiled
     assert igc.igc_tune_supported((256, 256, 64, 2, 6)) == 0
-    assert igc.igc_tune_supported((256, 256, 32, 4, 8, 8)) == 0  # no 8x8 MFMA block
+    assert igc.igc_tune_supported((256, 256, 32, 4, 8, 8, 0, 4)) == 0  # no 8x8 MFMA block
     # mfma 0 selects the 32x32x16 instance
-    assert igc.igc_tune_supported((256, 256, 32, 5, 8, 0)) == 1
-    assert igc.igc_tune_supported((256, 256, 32, 5, 8, 16)) == 0  # 5 stages x 1 k-step: odd fragment parity
+    assert igc.igc_tune_supported((256, 256, 32, 5, 8, 0, 0, 4)) == 1
+    assert igc.igc_tune_supported((256, 256, 32, 5, 8, 16, 0, 4)) == 0  # 5 stages x 1 k-step: odd fragment parity
 
 
-@pytest.mark.parametrize("shape,conv,expect", [
-    ((8192, 8192, 8192), 0, ((256, 256, 32, 4, 8, 16, 0, 4), 1, 0)),   # 1024 tiles of 256x256: data-parallel
-    ((100352, 256, 2304), 1, ((256, 256, 32, 4, 8, 16, 0, 4), 1, 0)),  # the 3x3 conv's GEMM view
-    ((100352, 256, 2304), 0, ((256, 256, 32, 4, 8, 16, 0, 4), 1, 0)),  # the same shape as a GEMM
-    ((2048, 1024, 16384), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 128 tiles of 128x128: stream-K
-    ((1000, 1000, 65536), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 256)),  # 64 tiles
-    ((1000, 1000, 3000), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),    # too little K to share
-    ((100352, 64, 256), 1, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),    # 1x1 conv with 64 outputs: 128-wide tiles
-    ((128, 96, 200), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),
-    ((0, 5, 7), 0, ((128, 128, 64, 4, 4, 32, 0, 4), 1, 0)),
+BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)
+
+
+@pytest.mark.parametrize("shape,op,expect", [
+    ((8192, 8192, 8192), igc.OP_GEMM, (BIG, 1, 0, 0)),              # 1024 tiles of 256x256: data-parallel
+    ((100352, 256, 2304), igc.OP_CONV_FPROP, (BIG, 1, 256, 1)),     # the 3x3 conv's GEMM view: 392 tiles = 1.53
+    ((100352, 256, 2304), igc.OP_CONV_DGRAD, (BIG, 1, 256, 1)),     # rounds, so 256 whole tiles then stream-K
+    ((100352, 256, 2304), igc.OP_GEMM, (BIG, 1, 256, 1)),
+    ((100352, 256, 512), igc.OP_GEMM, (BIG, 1, 0, 0)),              # too little K to split the last round
+    ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (BIG, 1, 0, 0)),      # last round 99% full: data-parallel
+    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (SMALL, 1, 256, 0)),   # the conv's filter gradient: 36 tiles, deep K
+    ((2048, 1024, 16384), igc.OP_GEMM, (SMALL, 1, 256, 0)),         # 128 tiles of 128x128: stream-K
+    ((1000, 1000, 65536), igc.OP_GEMM, (SMALL, 1, 256, 0)),         # 64 tiles
+    ((1000, 1000, 3000), igc.OP_GEMM, (SMALL, 1, 0, 0)),            # too little K to share
+    ((100352, 64, 256), igc.OP_CONV_FPROP, (SMALL, 1, 0, 0)),       # 1x1 conv with 64 outputs: 128-wide tiles
+    ((128, 96, 200), igc.OP_GEMM, (SMALL, 1, 0, 0)),
+    ((0, 5, 7), igc.OP_GEMM, (SMALL, 1, 0, 0)),
 ])
-def test_default_tune(shape, conv, expect):
-    t = igc.igc_default_tune(*shape, conv=conv)
-    assert (t.astuple(), t.k_splits, t.stream_k) == expect
+def test_default_tune(shape, op, expect):
+    t = igc.igc_default_tune(*shape, op=op)
+    assert (t.astuple(), t.k_splits, t.stream_k, t.sk_hybrid) == expect
     assert igc.igc_tune_supported(t) == 1
+
+
+def test_workspace_bytes():
+    """Workspace = one fp32 BM x BN partial tile per stream-K workgroup plus one int flag each (each part rounded
+    to 256 bytes), or S fp32 partial outputs (rows rounded to 4 floats) for a K split; nothing otherwise."""
+    ws = igc.igc_workspace_bytes
+    assert ws(igc.OP_GEMM, 8192, 8192, 8192) == 0
+    assert ws(igc.OP_GEMM, 2048, 1024, 16384) == 256 * 128 * 128 * 4 + 1024
+    assert ws(igc.OP_CONV_FPROP, 100352, 256, 2304) == 256 * 256 * 256 * 4 + 1024
+    assert ws(igc.OP_GEMM, 1000, 1000, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
+    assert ws(igc.OP_GEMM, 1000, 998, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
+    # stream-K with fewer K units than workgroups: G clamps to the units (2 tiles x 1 unit of 256)
+    assert ws(igc.OP_GEMM, 256, 128, 200, (128, 128, 64, 4, 4, 32, 0, 4, 1, 100)) == 2 * 128 * 128 * 4 + 256
+    # hybrid whose tiles fill whole rounds: no tile is split, no workspace
+    assert ws(igc.OP_GEMM, 256 * 16, 256 * 16, 4096, (256, 256, 32, 4, 8, 16, 0, 4, 1, 256, 0, 1)) == 0
+    assert ws(igc.OP_GEMM, 0, 5, 7) == 0
+    assert ws(igc.OP_GEMM, -1, 5, 7) == -1
+    assert ws(7, 5, 5, 7) == -1
+
+
+def test_no_pool_allocation_before_any_call():
+    assert igc.igc_pool_allocations() == 0
 
 
 ISSUE, WAIT, READ, BARRIER = 0, 1, 2, 3

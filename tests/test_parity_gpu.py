@@ -16,21 +16,31 @@ import torch
 import implicit_gemm_conv_amd as igc
 from implicit_gemm_conv_amd import inputs
 import oracle
-from gpu_util import (LAYOUT, assert_close, oracle_gemm, round_to, run_conv, run_gemm, say)
+from gpu_util import (LAYOUT, assert_close, oracle_gemm, round_to, run_conv, run_gemm, say, synchronize)
 
 pytestmark = pytest.mark.gpu
 
 NAN_BITS = {"bf16": 0x7FC0, "fp16": 0x7E00}
 
 
-def _compiled_tunes():
+def _compiled_tunes(full_only=False):
     try:
-        return igc.tunes()
+        return igc.tunes(full_only)
     except Exception:  # library not built: the GPU tests fail in the fixture below
-        return [(256, 256, 32, 5, 8)]
+        return [(256, 256, 32, 4, 8, 16, 0, 4, 0)]
 
 
 ALL_TUNES = _compiled_tunes()
+FULL_TUNES = set(_compiled_tunes(True))
+BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)
+
+
+def supports(tune, la="row", K=64, op="gemm"):
+    """A configuration built for every type, layout and operation supports any call; a study configuration only
+    GEMMs with row-major A and K % 8 == 0, and forward convolutions (checked by the caller's shapes)."""
+    if tuple(tune[:9]) in FULL_TUNES:
+        return True
+    return op in ("gemm", "fprop") and la == "row" and K % 8 == 0
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -201,18 +211,17 @@ def test_k_chain_tags(tune):
         assert np.all(y == float(tags.sum())), f"k-chain tune={tune} K={K}: {np.unique(y)[:5]}"
 
 
-@pytest.mark.parametrize("tune", [(128, 128, 64, 4, 4, 32, 0, 0), (256, 256, 32, 4, 8, 32, 0, 0),
-                                  (256, 128, 64, 3, 4, 32, 0, 0), (256, 256, 32, 4, 8, 16, 0, 0),
-                                  (128, 128, 64, 4, 4, 16, 0, 0), (256, 256, 64, 2, 8, 16, 1, 4),
-                                  (256, 256, 32, 4, 8, 16, 0, 4)])
+@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
 def test_split_k(tune):
     """K split over 2..8 workgroups per tile, fp32 partials summed in split order: ragged K, every layout."""
     cases = [(300, 270, 1000, "row", "row", 2, "f32", "bf16"), (257, 129, 777, "row", "col", 3, "bf16", "bf16"),
              (130, 200, 4096, "col", "row", 5, "f16", "fp16"), (64, 72, 200, "col", "col", 8, "f32", "bf16"),
              (1000, 1000, 6144, "row", "row", 4, "f32", "fp16")]
     for (M, N, K, la, lb, S, out, dtype) in cases:
+        if not supports(tune, la, K):
+            continue
         say(f"split-K tune {tune} S={S} {M}x{N}x{K} {la}/{lb} {dtype}->{out}")
-        gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=300 + S, tune=tuple(tune) + (S,))
+        gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=300 + S, tune=igc.tune(tune, k_splits=S))
 
 
 def test_split_k_deterministic_and_exact():
@@ -220,7 +229,7 @@ def test_split_k_deterministic_and_exact():
     oracle bit for bit and repeats bit for bit."""
     M, N, K = 384, 256, 3000
     A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", 3000, 256, "bf16", ("int", 4), ("int", 4), seed=8)
-    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=(128, 128, 64, 4, 4, 32, 0, 0, 6))[0]
+    outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32", tune=igc.tune(SMALL, k_splits=6))[0]
             for _ in range(2)]
     ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row")
     assert np.array_equal(outs[0], ref) and np.array_equal(outs[0], outs[1])
@@ -231,17 +240,12 @@ def test_conv_split_k():
     x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=41)
     for S in (2, 3):
         say(f"conv split-K S={S}")
-        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=(128, 128, 64, 4, 4, 32, 0, 0, S))
+        y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=igc.tune(SMALL, k_splits=S))
         ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
         assert_close(y, ref, Sabs, "bf16", f"conv split {S}")
 
 
-SK_TUNES = [(256, 256, 32, 4, 8, 16, 0, 0), (128, 128, 64, 4, 4, 32, 0, 0), (256, 256, 64, 2, 4, 32, 1, 0),
-            (256, 256, 32, 5, 8, 32, 0, 0), (256, 256, 64, 1, 4, 32, 0, 0), (256, 256, 64, 2, 8, 16, 1, 4),
-            (256, 256, 32, 4, 8, 16, 0, 4)]
-
-
-@pytest.mark.parametrize("tune", SK_TUNES)
+@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
 def test_stream_k(tune):
     """Stream-K over G persistent workgroups: runs that start and end inside tiles, runs inside one tile, more
     workgroups than K units (G clamps), ragged K, every layout and dtype."""
@@ -249,8 +253,28 @@ def test_stream_k(tune):
              (520, 390, 4096, "col", "row", 64, "f16", "fp16"), (64, 72, 200, "col", "col", 300, "f32", "bf16"),
              (1000, 1000, 6144, "row", "row", 256, "f32", "fp16"), (513, 777, 2304, "row", "row", 33, "f32", "bf16")]
     for (M, N, K, la, lb, G, out, dtype) in cases:
+        if not supports(tune, la, K):
+            continue
         say(f"stream-K tune {tune} G={G} {M}x{N}x{K} {la}/{lb} {dtype}->{out}")
-        gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=400 + G, tune=tuple(tune) + (1, G))
+        gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=400 + G, tune=igc.tune(tune, stream_k=G))
+
+
+@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
+def test_stream_k_hybrid(tune):
+    """Whole tiles in data-parallel rounds of G, then stream-K over the tiles of the last, partial round: more
+    tiles than workgroups, a tail shorter than G, tails with whole-tile runs, ragged K."""
+    bm, bn = tune[0], tune[1]
+    cases = [(5 * bm + 17, 3 * bn + 9, 1000, 7, "bf16", "row", "f32"),    # 18 tiles: 2 rounds of 7, 4-tile tail
+             (4 * bm, 2 * bn, 2048, 3, "bf16", "row", "bf16"),            # 8 tiles: 2 rounds of 3, 2-tile tail
+             (3 * bm, 3 * bn, 1536, 4, "fp16", "col", "f16"),             # 9 tiles: 2 rounds, 1-tile tail
+             (2 * bm, 2 * bn, 4096, 2, "bf16", "row", "f32"),             # 4 tiles = 2 whole rounds: no split
+             (2 * bm + 1, bn, 777, 2, "bf16", "row", "f32")]              # ragged K
+    for (M, N, K, G, dtype, lb, out) in cases:
+        if not supports(tune, "row", K):
+            continue
+        say(f"hybrid stream-K tune {tune} G={G} {M}x{N}x{K} row/{lb} {dtype}->{out}")
+        gemm_case(M, N, K, "row", lb, dtype=dtype, out=out, seed=500 + G,
+                  tune=igc.tune(tune, stream_k=G, sk_hybrid=1))
 
 
 def test_stream_k_deterministic_and_exact():
@@ -261,7 +285,7 @@ def test_stream_k_deterministic_and_exact():
     ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row")
     for G in (5, 37, 256):
         outs = [run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out="f32",
-                         tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, G))[0] for _ in range(2)]
+                         tune=igc.tune(BIG, stream_k=G))[0] for _ in range(2)]
         assert np.array_equal(outs[0], ref) and np.array_equal(outs[0], outs[1]), f"G={G}"
     M, N, K = 520, 136, 2400
     A = np.full((M, K), 0x3F80, np.uint16)
@@ -269,7 +293,7 @@ def test_stream_k_deterministic_and_exact():
     Bt = torch.from_numpy(np.repeat(tags[:, None], N, axis=1)).to(torch.bfloat16).view(torch.int16).numpy()
     for G in (3, 11, 100):
         y, _ = run_gemm(M, N, K, A, K, "row", Bt.view(np.uint16), N, "row", out="f32",
-                        tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, G))
+                        tune=igc.tune(BIG, stream_k=G))
         assert np.all(y == float(tags.sum())), f"k-chain stream-K G={G}: {np.unique(y)[:5]}"
 
 
@@ -277,7 +301,7 @@ def test_stream_k_rejects_mixed_with_split():
     A = torch.zeros(64 * 64, dtype=torch.int16, device="cuda")
     C = torch.zeros(64 * 64, dtype=torch.float32, device="cuda")
     st = igc.gemm_bf16_ex(64, 64, 64, A, 64, igc.ROW_MAJOR, A, 64, igc.ROW_MAJOR, C, 64, igc.OUT_F32,
-                          (256, 256, 32, 4, 8, 16, 0, 0, 2, 8))
+                          igc.tune(BIG, k_splits=2, stream_k=8))
     assert st == igc.IGC_ERR_INVALID_VALUE
 
 
@@ -285,16 +309,17 @@ def test_conv_stream_k():
     N, H, W, C, K = 2, 9, 7, 256, 136
     x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=43)
     ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
-    for tune in ((256, 256, 32, 4, 8, 16, 0, 0, 1, 5), (256, 256, 32, 4, 8, 32, 0, 0, 1, 3),
-                 (128, 128, 64, 4, 4, 32, 0, 0, 1, 7), (256, 256, 64, 2, 8, 16, 1, 4, 1, 9)):
-        say(f"conv stream-K {tune}")
+    for tune in (igc.tune(BIG, stream_k=5), igc.tune((256, 256, 32, 4, 8, 32, 0, 4), stream_k=3),
+                 igc.tune(SMALL, stream_k=7), igc.tune((256, 256, 64, 2, 8, 16, 1, 4), stream_k=9),
+                 igc.tune(BIG, stream_k=3, sk_hybrid=1)):
+        say(f"conv stream-K {tune.astuple()} G={tune.stream_k} hybrid={tune.sk_hybrid}")
         y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="bf16", tune=tune)
-        assert_close(y, ref, Sabs, "bf16", f"conv stream-K {tune}")
+        assert_close(y, ref, Sabs, "bf16", f"conv stream-K {tune.astuple()}")
     # channels not a multiple of the K tile: per-lane tap split inside each run
     N, H, W, C, K = 1, 8, 6, 24, 40
     x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=44)
     ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
-    y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="f32", tune=(256, 256, 32, 4, 8, 16, 0, 0, 1, 2))
+    y, _ = run_conv(N, H, W, C, K, 3, 3, x, w, ph=1, pw=1, out="f32", tune=igc.tune(BIG, stream_k=2))
     assert_close(y, ref, Sabs, "f32", "conv stream-K C=24")
 
 
@@ -427,8 +452,8 @@ def test_output_epilogue_exact(tune, stream_k):
     for i, (dtype, out) in enumerate((("bf16", "bf16"), ("fp16", "f16"), ("bf16", "f32"))):
         A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", K, N, dtype, ("int", 4), ("int", 4),
                                               seed=40 + i)
-        t = tuple(tune[:8]) + (1, stream_k)
-        say(f"epilogue {M}x{N}x{K} {dtype}->{out} tune={t}")
+        t = igc.tune(tune, stream_k=stream_k)
+        say(f"epilogue {M}x{N}x{K} {dtype}->{out} tune={tune} stream_k={stream_k}")
         y, _ = run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out=out, dtype=dtype, ldc=N + 8, tune=t)
         ref, _ = oracle_gemm(M, N, K, A, lda, "row", B, ldb, "row", dtype)
         bad = np.count_nonzero(y != round_to(ref, out))
