@@ -23,7 +23,7 @@ OP_GEMM, OP_CONV_FPROP, OP_CONV_DGRAD, OP_CONV_WGRAD = range(4)
 
 # Every exported entry point (include/igc.h), for the load check.
 EXPORTS = (
-    "gemm_bf16", "gemm_fp16", "gemm_bf16_ex", "gemm_fp16_ex",
+    "gemm_bf16", "gemm_fp16", "gemm_bf16_ex", "gemm_fp16_ex", "gemm_bf16_noalloc",
     "conv2d_nhwc_implicit_gemm", "conv2d_nhwc_implicit_gemm_fp16", "conv2d_nhwc_implicit_gemm_ex",
     "conv2d_nhwc_implicit_gemm_fp16_ex",
     "conv2d_nhwc_dgrad_implicit_gemm", "conv2d_nhwc_dgrad_implicit_gemm_fp16", "conv2d_nhwc_dgrad_implicit_gemm_ex",
@@ -83,7 +83,7 @@ def lib():
         tp = ctypes.POINTER(Tune)
         gemm = [i64, i64, i64, p, i64, i32, p, i64, i32, p, i64, i32]
         conv = [i32] * 13 + [p, p, p, i32]
-        protos = {"gemm_bf16": gemm + [p], "gemm_fp16": gemm + [p],
+        protos = {"gemm_bf16": gemm + [p], "gemm_fp16": gemm + [p], "gemm_bf16_noalloc": gemm + [p],
                   "gemm_bf16_ex": gemm + [tp, p, i64, p], "gemm_fp16_ex": gemm + [tp, p, i64, p]}
         for base in ("conv2d_nhwc_implicit_gemm", "conv2d_nhwc_dgrad_implicit_gemm", "conv2d_nhwc_wgrad_implicit_gemm"):
             protos[base] = conv + [p]
@@ -164,6 +164,11 @@ def gemm_bf16(M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, stream=None):
 
 def gemm_fp16(M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, stream=None):
     return lib().gemm_fp16(M, N, K, _ptr(A), lda, la, _ptr(B), ldb, lb, _ptr(C), ldc, c_type, _stream(stream))
+
+
+def gemm_bf16_noalloc(M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, stream=None):
+    return lib().gemm_bf16_noalloc(M, N, K, _ptr(A), lda, la, _ptr(B), ldb, lb, _ptr(C), ldc, c_type,
+                                   _stream(stream))
 
 
 def gemm_bf16_ex(M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, tune=None, workspace=None, workspace_bytes=None,

@@ -28,6 +28,14 @@
 // to 1 (and writes its tile as NaN).  Each GPU holds its own copy.
 static __device__ __align__(256) int g_err_word;
 
+// Workspace of gemm_bf16_noalloc, for callers that cannot allocate: room for
+// the partial tiles and flags of a stream-K schedule of 256 workgroups with
+// 256 x 256 tiles, the largest schedule the built-in choice makes.  Each GPU
+// the library runs on holds its own copy until the process ends; calls that
+// overlap on one GPU share it and race.
+constexpr int64_t kScratchBytes = (64ll << 20) + 4096;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace igc {
 
 constexpr int kMaxDevices = 64;
@@ -47,6 +55,25 @@ static int* err_word_ptr() {
         tried[dev] = true;
         void* ptr = nullptr;
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_err_word)) == hipSuccess) ptrs[dev] = (int*)ptr;
+        (void)hipGetLastError();
+    }
+    return ptrs[dev];
+}
+
+// The current device's copy of `scratch`, looked up once per device with that
+// device current (the array's name is only a host-side stand-in); nullptr if
+// the lookup failed.
+static void* scratch_ptr() {
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices];
+    static bool tried[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!tried[dev]) {
+        tried[dev] = true;
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) ptrs[dev] = ptr;
         (void)hipGetLastError();
     }
     return ptrs[dev];
@@ -509,6 +536,19 @@ igc_status_t conv2d_nhwc_wgrad_implicit_gemm_fp16_ex(int N, int H, int W, int C,
                                                      int64_t workspace_bytes, igc_stream_t stream) {
     return conv_any(OP_WGRAD, true, N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, x, dy, dw,
                     dw_type, tune, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+igc_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, igc_layout_t la,
+                               const void* B, int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type,
+                               igc_stream_t stream) {
+    // the built-in schedule, with its workspace in this device's scratch array
+    if (M < 0 || N < 0 || K < 0) return IGC_ERR_INVALID_VALUE;
+    const Plan pl = pick(nullptr, false, la == IGC_ROW_MAJOR, lb == IGC_COL_MAJOR, OP_GEMM, M, N, K);
+    if (pl.inst && layout_of(pl, M, N, K).bytes > kScratchBytes) return IGC_ERR_UNSUPPORTED;
+    void* ws = scratch_ptr();
+    if (!ws) return IGC_ERR_HIP;
+    return gemm_any(false, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, nullptr, ws, kScratchBytes,
+                    (hipStream_t)stream);
 }
 
 int64_t igc_workspace_bytes(igc_op_t op, int64_t M, int64_t N, int64_t K, const igc_tune_t* tune) {

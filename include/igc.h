@@ -252,6 +252,19 @@ igc_status_t conv2d_nhwc_wgrad_implicit_gemm_fp16_ex(int N, int H, int W, int C,
                                                      igc_out_t dw_type, const igc_tune_t *tune, void *workspace,
                                                      int64_t workspace_bytes, igc_stream_t stream);
 
+/* gemm_bf16 for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the built-in
+ * schedule, with its workspace (stream-K partial tiles and flags) in a
+ * library-owned device array of 64 MiB + 4 KiB that each GPU holds until the
+ * process ends.  The call allocates nothing and gives the same bits as
+ * gemm_bf16.  Calls that overlap on one GPU share the array and race: order
+ * them (one stream).  A shape whose schedule needs more than the array holds is
+ * IGC_ERR_UNSUPPORTED (the built-in choice never does); IGC_ERR_HIP if the
+ * array cannot be located on the current device; otherwise as gemm_bf16. */
+igc_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, igc_layout_t la,
+                               const void *B, int64_t ldb, igc_layout_t lb, void *C, int64_t ldc, igc_out_t c_type,
+                               igc_stream_t stream);
+
 /* Workspace bytes a call needs for operation `op` with GEMM view M x N x K
  * (see each operation above) under `tune` (NULL: the built-in choice): 0 when
  * the schedule does not split K.  Returns -1 for negative sizes, a bad op or
