@@ -117,8 +117,9 @@ def workload_cost(c):
     if c["kind"] == "gemm":
         return gemm_flops(c), 2 * (c["M"] * c["K"] + c["K"] * c["N"]) + out_bytes * c["M"] * c["N"]
     P, Q = conv_geometry(c)
-    return conv_flops(c), (2 * (c["N"] * c["H"] * c["W"] * c["C"] + c["K"] * c["R"] * c["S"] * c["C"]) +
-                           out_bytes * c["N"] * P * Q * c["K"])
+    x, w, y = c["N"] * c["H"] * c["W"] * c["C"], c["K"] * c["R"] * c["S"] * c["C"], c["N"] * P * Q * c["K"]
+    ins, out = {"conv": (x + w, y), "dgrad": (y + w, x), "wgrad": (x + y, w)}[c["kind"]]
+    return conv_flops(c), 2 * ins + out_bytes * out
 
 
 def run_suite(reps, warmup):
@@ -139,16 +140,20 @@ def run_suite(reps, warmup):
                                         igc.OUT_CODES[c["out"]], stream=stream))
             t = igc.igc_default_tune(c["M"], c["N"], c["K"])
         else:
-            x, w = inputs.workload_operands(name)
+            a0, a1 = inputs.workload_operands(name)
             P, Q = conv_geometry(c)
-            dx = torch.from_numpy(x.view(np.int16)).cuda()
-            dw = torch.from_numpy(w.view(np.int16)).cuda()
-            dy = torch.empty((c["N"] * P * Q * c["K"],), dtype=out_dt, device="cuda")
-            cfn = igc.conv2d_nhwc_implicit_gemm_fp16_ex if c["dtype"] == "fp16" else igc.conv2d_nhwc_implicit_gemm_ex
+            d0 = torch.from_numpy(a0.view(np.int16)).cuda()
+            d1 = torch.from_numpy(a1.view(np.int16)).cuda()
+            op, cfn = {"conv": (igc.OP_CONV_FPROP, igc.conv2d_nhwc_implicit_gemm),
+                       "dgrad": (igc.OP_CONV_DGRAD, igc.conv2d_nhwc_dgrad_implicit_gemm),
+                       "wgrad": (igc.OP_CONV_WGRAD, igc.conv2d_nhwc_wgrad_implicit_gemm)}[c["kind"]]
+            view = igc.conv_gemm_view(op, c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"],
+                                      c["ph"], c["pw"], c["dh"], c["dw"])
+            dy = torch.empty((view[0] * view[1],), dtype=out_dt, device="cuda")
             call = lambda: igc.check(cfn(
                 c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"], c["ph"], c["pw"], c["dh"],
-                c["dw"], dx, dw, dy, igc.OUT_CODES[c["out"]], stream=stream))
-            t = igc.igc_default_tune(c["N"] * P * Q, c["K"], c["R"] * c["S"] * c["C"], op=igc.OP_CONV_FPROP)
+                c["dw"], d0, d1, dy, igc.OUT_CODES[c["out"]], stream=stream))
+            t = igc.igc_default_tune(*view, op=op)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()

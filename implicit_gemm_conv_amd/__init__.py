@@ -31,7 +31,7 @@ EXPORTS = (
     "conv2d_nhwc_wgrad_implicit_gemm", "conv2d_nhwc_wgrad_implicit_gemm_fp16", "conv2d_nhwc_wgrad_implicit_gemm_ex",
     "conv2d_nhwc_wgrad_implicit_gemm_fp16_ex",
     "igc_workspace_bytes", "igc_tune_supported", "igc_default_tune", "igc_tune_count", "igc_tune_get",
-    "igc_tune_full", "igc_tune_lds_bytes", "igc_status_string", "igc_take_device_error", "igc_debug_stream_k",
+    "igc_tune_scope", "igc_tune_lds_bytes", "igc_status_string", "igc_take_device_error", "igc_debug_stream_k",
     "igc_pool_allocations", "igc_ring_schedule", "igc_lds_chunk",
 )
 
@@ -104,8 +104,8 @@ def lib():
         L.igc_tune_count.restype = i32
         L.igc_tune_get.argtypes = [i32, tp]
         L.igc_tune_get.restype = i32
-        L.igc_tune_full.argtypes = [i32]
-        L.igc_tune_full.restype = i32
+        L.igc_tune_scope.argtypes = [i32]
+        L.igc_tune_scope.restype = i32
         L.igc_tune_lds_bytes.argtypes = [tp]
         L.igc_tune_lds_bytes.restype = i64
         L.igc_status_string.argtypes = [i32]
@@ -260,18 +260,21 @@ def igc_tune_get(i):
     return t if lib().igc_tune_get(i, ctypes.byref(t)) else None
 
 
-def igc_tune_full(i):
-    return lib().igc_tune_full(i)
+SCOPE_ALL, SCOPE_STREAM_K = 1, 2
+
+
+def igc_tune_scope(i):
+    return lib().igc_tune_scope(i)
 
 
 def igc_tune_lds_bytes(t):
     return lib().igc_tune_lds_bytes(_tune(t))
 
 
-def tunes(full_only=False):
-    """Compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves, ring_sync) configurations (only
-    those built for every input type, layout and operation when full_only)."""
-    return [igc_tune_get(i).astuple() for i in range(igc_tune_count()) if not full_only or igc_tune_full(i)]
+def tunes(scope=0):
+    """Compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves, ring_sync) configurations whose
+    scope includes every bit of `scope` (SCOPE_ALL: every type, layout and operation; SCOPE_STREAM_K)."""
+    return [igc_tune_get(i).astuple() for i in range(igc_tune_count()) if igc_tune_scope(i) & scope == scope]
 
 
 def igc_status_string(status):

@@ -35,7 +35,7 @@ FAMILIES_STUDY = (0, 1, 2)        # bf16 and fp16 GEMM (row-major A), bf16 forwa
 
 
 def tile_configs():
-    """(bm, bn, bk, depth, waves, mfma, half, loaders, sync, full) per X(...) line of tile_configs.hpp."""
+    """(bm, bn, bk, depth, waves, mfma, half, loaders, sync, scope) per X(...) line of tile_configs.hpp."""
     text = open(os.path.join(CSRC, "tile_configs.hpp")).read()
     rows = re.findall(r"^\s*X\(([\d,\s]+)\)", text, re.M)
     out = []
@@ -60,14 +60,16 @@ def instance_units(configs=None):
     # IGC_BUILD_ONLY="256x256x32x4x8x16x0x4x0,..." builds a subset of the configurations (a quick partial build
     # while working on one tile; the others then report IGC_ERR_UNSUPPORTED)
     only = [c for c in os.environ.get("IGC_BUILD_ONLY", "").split(",") if c]
-    for (bm, bn, bk, d, w, mi, h, lw, sy, full) in (configs or tile_configs()):
+    for (bm, bn, bk, d, w, mi, h, lw, sy, scope) in (configs or tile_configs()):
         if only and f"{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}x{lw}x{sy}" not in only:
             continue
+        full, sk = scope & 1, (scope >> 1) & 1
         for fam in (FAMILIES_FULL if full else FAMILIES_STUDY):
             obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}x{lw}x{sy}_f{fam}.o")
             units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}",
                           f"-DIGC_W={w}", f"-DIGC_MI={mi}", f"-DIGC_HALF={h}", f"-DIGC_LW={lw}", f"-DIGC_SYNC={sy}",
-                          f"-DIGC_FULL={full}", f"-DIGC_FAMILY={fam}", "-c", os.path.join(CSRC, "instances.hip"),
+                          f"-DIGC_FULL={full}", f"-DIGC_SK={sk}", f"-DIGC_FAMILY={fam}", "-c",
+                          os.path.join(CSRC, "instances.hip"),
                           "-o", obj])
     return units
 

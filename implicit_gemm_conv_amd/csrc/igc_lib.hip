@@ -29,11 +29,12 @@
 static __device__ __align__(256) int g_err_word;
 
 // Workspace of gemm_bf16_noalloc, for callers that cannot allocate: room for
-// the partial tiles and flags of a stream-K schedule of 256 workgroups with
-// 256 x 256 tiles, the largest schedule the built-in choice makes.  Each GPU
-// the library runs on holds its own copy until the process ends; calls that
-// overlap on one GPU share it and race.
-constexpr int64_t kScratchBytes = (64ll << 20) + 4096;
+// the largest workspace the built-in choice asks for (stream-K over 256
+// workgroups of 128 x 128 fp32 partials, 16 MiB + 1 KiB, or a 2-way split of at
+// most 128 tiles of 128 x 128, 16 MiB).  Each GPU the library runs on holds its
+// own copy until the process ends; calls that overlap on one GPU share it and
+// race.
+constexpr int64_t kScratchBytes = (16ll << 20) + 4096;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace igc {
@@ -196,6 +197,17 @@ static Layout layout_of(const Plan& pl, int64_t M, int64_t N, int64_t K) {
     return L;
 }
 
+// The loop variant (kernel) a call needs: the convolutions' gathered operand
+// uses per-pixel tap masks when the filter fits 16 x 16 (and, for the data
+// gradient, the stride is 1), whole taps per K tile when the gathered channel
+// count is a multiple of BK; a GEMM with K % 8 != 0 needs the ragged loop.
+static int loop_variant(const Params& p, const Instance* inst) {
+    if (inst->op == OP_FPROP || inst->op == OP_DGRAD)
+        return !p.conv_masks ? CONV_GENERIC : (p.conv_uniform ? UNIFORM_TAP : PLAIN);
+    if (inst->op == OP_WGRAD) return PLAIN;
+    return p.k_ragged8 ? RAGGED : PLAIN;
+}
+
 // Launches the mainloop (and, for a K split, the fixed-order reduction; for
 // stream-K, the flag clearing before it).  The workspace is the caller's, or
 // taken from the library's pool and released with hipFreeAsync after the work
@@ -205,6 +217,8 @@ static igc_status_t launch(const Plan& pl, Params p, void* user_ws, int64_t user
     const Layout L = layout_of(pl, p.M, p.N, p.K);
     if (L.tiles <= 0) return IGC_OK;
     if (L.tiles * L.S > 0x7fffffff) return IGC_ERR_UNSUPPORTED;
+    // a configuration built without this loop variant or without stream-K kernels
+    if (!(L.G > 0 ? inst->fn_sk : inst->fn)[loop_variant(p, inst)]) return IGC_ERR_UNSUPPORTED;
     if (user_ws && (user_ws_bytes < L.bytes || (reinterpret_cast<uintptr_t>(user_ws) & 255u)))
         return IGC_ERR_INVALID_VALUE;
     int* err = err_word_ptr();
@@ -219,6 +233,8 @@ static igc_status_t launch(const Plan& pl, Params p, void* user_ws, int64_t user
     }
     hipError_t e = hipSuccess;
     unsigned grid = 0;
+    const int v = loop_variant(p, inst);
+    const void* fn = L.G > 0 ? inst->fn_sk[v] : inst->fn[v];
     if (L.G > 0) {
         p.sk_grid = L.G;
         p.sk_units = L.UT;
@@ -246,7 +262,7 @@ static igc_status_t launch(const Plan& pl, Params p, void* user_ws, int64_t user
     if (e == hipSuccess) {
         Params arg = p;
         void* args[] = {&arg};
-        e = hipLaunchKernel(inst->fn, dim3(grid), dim3(64 * inst->waves), args, 0, stream);
+        e = hipLaunchKernel(fn, dim3(grid), dim3(64 * inst->waves), args, 0, stream);
     }
     if (e == hipSuccess && L.G == 0 && L.S > 1)
         e = launch_split_reduce(p.ws, L.S, p.ws_stride, p.M, p.N, p.ldws, p.C, p.ldc, p.out_kind, stream);
@@ -281,7 +297,6 @@ static igc_status_t gemm_any(bool fp16, int64_t M, int64_t N, int64_t K, const v
         if (!b_kc && (inst->bk * ldb + inst->bn) * 2 >= 0x7fffffffLL) return IGC_ERR_UNSUPPORTED;
     }
     if (!aligned16(C) || (ldc * out_size(ct)) % 16 != 0) return IGC_ERR_MISALIGNED;
-    if (!inst->full && K % 8 != 0) return IGC_ERR_UNSUPPORTED;  // a study kernel has no ragged-K loop
     if ((M + inst->bm - 1) / inst->bm > 0x7fffffff || (N + inst->bn - 1) / inst->bn > 0x7fffffff)
         return IGC_ERR_UNSUPPORTED;
 
@@ -401,8 +416,6 @@ static igc_status_t conv_any(int op, bool fp16, int N, int H, int W, int C, int 
     p.cin_magic = fastdiv_magic((uint32_t)(p.gC > 0 ? p.gC : 1));
     p.s_magic = fastdiv_magic((uint32_t)S);
     p.tpt_magic = fastdiv_magic((uint32_t)p.tpt);
-    // a study kernel has only the whole-tap masked loop
-    if (!inst->full && op != OP_WGRAD && !(p.conv_uniform && p.conv_masks)) return IGC_ERR_UNSUPPORTED;
     p.q_magic = fastdiv_magic((uint32_t)Q);
     p.pq_magic = fastdiv_magic((uint32_t)(P * Q));
     return launch(pl, p, ws, ws_bytes, stream);
@@ -581,7 +594,7 @@ int igc_tune_get(int i, igc_tune_t* out) {
     return 1;
 }
 
-int igc_tune_full(int i) { return (i >= 0 && i < num_tunes() && tune_is_full(i)) ? 1 : 0; }
+int igc_tune_scope(int i) { return (i >= 0 && i < num_tunes()) ? tune_scope(i) : 0; }
 
 int64_t igc_tune_lds_bytes(const igc_tune_t* tune) {
     if (!tune) return 0;

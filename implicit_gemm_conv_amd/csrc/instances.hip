@@ -6,16 +6,18 @@
 //   2: forward convolution (bf16 and fp16; with IGC_FULL 0 bf16 only)
 //   3: data gradient (bf16 and fp16)
 //   4: filter gradient (bf16 and fp16)
-// and registers the table when the library is loaded.  With IGC_FULL 0 the
-// kernels carry only their main loop variant (K % 8 == 0 for the GEMM, whole
-// filter taps per K tile and filters of at most 16 x 16 for the convolution).
+// and registers the table when the library is loaded.  Every loop variant of
+// an instance is a kernel of its own; IGC_SK 1 also builds the stream-K
+// kernels.  With IGC_FULL 0 only the main loop variant is built (K % 8 == 0
+// for the GEMM, whole filter taps per K tile and filters of at most 16 x 16
+// for the convolution).
 #include "instances.hpp"
 #include "mainloop.hpp"
 
 #if !defined(IGC_BM) || !defined(IGC_BN) || !defined(IGC_BK) || !defined(IGC_D) || !defined(IGC_W) || \
     !defined(IGC_MI) || !defined(IGC_HALF) || !defined(IGC_LW) || !defined(IGC_SYNC) || !defined(IGC_FULL) || \
-    !defined(IGC_FAMILY)
-#error "compile with -DIGC_BM=.. -DIGC_BN=.. -DIGC_BK=.. -DIGC_D=.. -DIGC_W=.. -DIGC_MI=.. -DIGC_HALF=.. -DIGC_LW=.. -DIGC_SYNC=.. -DIGC_FULL=.. -DIGC_FAMILY=.."
+    !defined(IGC_SK) || !defined(IGC_FAMILY)
+#error "compile with -DIGC_BM=.. -DIGC_BN=.. -DIGC_BK=.. -DIGC_D=.. -DIGC_W=.. -DIGC_MI=.. -DIGC_HALF=.. -DIGC_LW=.. -DIGC_SYNC=.. -DIGC_FULL=.. -DIGC_SK=.. -DIGC_FAMILY=.."
 #endif
 
 namespace igc {
@@ -23,13 +25,31 @@ namespace igc {
 template <bool FP16, bool AKC, bool BKC, int OPK>
 using Here = Cfg<FP16, IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, IGC_LW, IGC_SYNC, AKC, BKC, OPK>;
 
-#define IGC_ENTRY(FP16, AKC, BKC, OPK)                                                                        \
-    Instance {                                                                                               \
-        IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, Here<FP16, AKC, BKC, OPK>::NL, IGC_SYNC, OPK, \
-            FP16, AKC, BKC, IGC_FULL != 0,                                                                  \
-            reinterpret_cast<const void*>(&gemm_kernel<Here<FP16, AKC, BKC, OPK>, IGC_FULL != 0>),           \
-            Here<FP16, AKC, BKC, OPK>::LDS_BYTES                                                             \
-    }
+// The kernel of loop variant V (stream-K when SK), or nullptr when the
+// operation has no such variant or this build leaves it out.
+template <class C, int V, bool SK>
+constexpr const void* kernel_of() {
+    if constexpr (!variant_applies<C, V>() || (!IGC_FULL && V != main_variant<C>()) || (SK && !IGC_SK))
+        return nullptr;
+    else if constexpr (SK)
+        return reinterpret_cast<const void*>(&gemm_sk_kernel<C, V>);
+    else
+        return reinterpret_cast<const void*>(&gemm_kernel<C, V>);
+}
+
+template <bool FP16, bool AKC, bool BKC, int OPK>
+Instance entry() {
+    using C = Here<FP16, AKC, BKC, OPK>;
+    return Instance{IGC_BM, IGC_BN, IGC_BK, IGC_D, IGC_W, IGC_MI, IGC_HALF, C::NL, IGC_SYNC, OPK, FP16, AKC, BKC,
+                    IGC_FULL != 0,
+                    {kernel_of<C, PLAIN, false>(), kernel_of<C, UNIFORM_TAP, false>(), kernel_of<C, RAGGED, false>(),
+                     kernel_of<C, CONV_GENERIC, false>()},
+                    {kernel_of<C, PLAIN, true>(), kernel_of<C, UNIFORM_TAP, true>(), kernel_of<C, RAGGED, true>(),
+                     kernel_of<C, CONV_GENERIC, true>()},
+                    C::LDS_BYTES};
+}
+
+#define IGC_ENTRY(FP16, AKC, BKC, OPK) entry<FP16, AKC, BKC, OPK>()
 
 static const Instance kTable[] = {
 #if IGC_FAMILY == 0

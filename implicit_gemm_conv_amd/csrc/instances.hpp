@@ -12,7 +12,9 @@ struct Instance {
     int op;              // OpKind: 0 GEMM, 1 forward conv, 2 data gradient, 3 filter gradient
     bool fp16, a_kc, b_kc;
     bool full;           // every loop variant compiled (else only K % 8 == 0 GEMMs and whole-tap convolutions)
-    const void* fn;      // __global__ gemm_kernel<Cfg<...>, full>
+    // kernels by loop variant (PLAIN, UNIFORM_TAP, RAGGED, CONV_GENERIC), nullptr where not built:
+    const void* fn[4];     // __global__ gemm_kernel<Cfg<...>, V>: data-parallel grid and split-K
+    const void* fn_sk[4];  // __global__ gemm_sk_kernel<Cfg<...>, V>: stream-K
     int64_t lds_bytes;   // static LDS of one workgroup
 };
 
@@ -24,6 +26,6 @@ const Instance* find_instance(const igc_tune_t& t, bool fp16, bool a_kc, bool b_
 igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op);
 int num_tunes();
 igc_tune_t tune_at(int i);
-bool tune_is_full(int i);
+int tune_scope(int i);
 
 }  // namespace igc

@@ -185,6 +185,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords, kRsrcFlags);
 }
 
+// A buffer resource whose base is pinned to scalar registers at its point of
+// use.  The base of every operand tile is uniform, but when the compiler
+// computes it in vector registers (a 64-bit product, or a value that register
+// pressure moved there) it must wrap each load in a waterfall loop; taking the
+// two address words through readfirstlane keeps the resource scalar.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void* base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, IGC_LDS void* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
 }
@@ -523,7 +535,7 @@ struct Mainloop {
         // ---- A
         if constexpr (OP == 0 && J1 > J0) {
             if constexpr (C::GATHER_A) {
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc_u(p.A);
                 // K index k = ((r*S + s) * gC + c): filter tap (r, s), channel c.
                 // This lane's chunk is the same logical chunk for all its loads.
                 int r, s, cin;
@@ -579,14 +591,14 @@ struct Mainloop {
                     });
                 }
             } else if constexpr (C::A_KC) {
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (m0 * p.lda + k0) * 2);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc_u((const char*)p.A + (m0 * p.lda + k0) * 2);
                 const bool kout = 8 * ca_lane >= krem;
                 static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     dma16(rs, sa + (j * C::NL + wave) * 1024, kout ? kOob : da.voff[j]);
                 });
             } else {
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.A + (k0 * p.lda + m0) * 2);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc_u((const char*)p.A + (k0 * p.lda + m0) * 2);
                 static_for<J0, J1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     const int q = j * C::NL + wave;
@@ -598,7 +610,7 @@ struct Mainloop {
         if constexpr (OP == 1 && J1 > J0) {
             constexpr int B0 = J0, B1 = J1;
             if constexpr (C::B_KC) {
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (n0 * p.ldb + k0) * 2);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc_u((const char*)p.B + (n0 * p.ldb + k0) * 2);
                 const bool kout = 8 * cb_lane >= krem;
                 static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
@@ -609,17 +621,21 @@ struct Mainloop {
                 const int RS = p.R * p.S;
                 if constexpr (kUniformTap) {
                     // the tile lies in one tap: rows kc0 .. kc0+BK-1 are ldb = R*S*Cin apart
+                    // 32-bit scalar arithmetic (the filter spans < 2^31 bytes), made explicitly
+                    // uniform: a base computed in vector registers would force a waterfall loop
+                    // around every load of the tile
                     const uint32_t tap = fastdiv((uint32_t)k0, (uint32_t)p.gC, p.cin_magic);
-                    const int64_t kc0 = k0 - (int64_t)tap * p.gC;
-                    const __amdgpu_buffer_rsrc_t rs =
-                        make_rsrc((const char*)p.B + ((kc0 * RS + tap) * p.N + n0) * 2);
+                    const uint32_t kc0 = (uint32_t)k0 - tap * (uint32_t)p.gC;
+                    const uint32_t base = __builtin_amdgcn_readfirstlane(
+                        ((kc0 * (uint32_t)RS + tap) * (uint32_t)p.N + (uint32_t)n0) * 2u);
+                    const __amdgpu_buffer_rsrc_t rs = make_rsrc_u((const char*)p.B + base);
                     static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                         constexpr int j = J;
                         const int q = j * C::NL + wave;
                         dma16(rs, sb + q * 1024, TB::row_of(q, lane) >= krem ? kOob : db.voff[j]);
                     });
                 } else {
-                    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + n0 * 2);
+                    const __amdgpu_buffer_rsrc_t rs = make_rsrc_u((const char*)p.B + n0 * 2);
                     static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                         constexpr int j = J;
                         const int q = j * C::NL + wave;
@@ -634,7 +650,7 @@ struct Mainloop {
             } else if constexpr (C::WGRAD) {
                 // K row k0 + i = output pixel (n, p, q); its window's tap (r, s)
                 // reads x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][channel]
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.B);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc_u(p.B);
                 const uint32_t PQ = (uint32_t)(p.P * p.Q);
                 static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
@@ -654,7 +670,7 @@ struct Mainloop {
                     dma16(rs, sb + q * 1024, ok ? off : kOob);
                 });
             } else {
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)p.B + (k0 * p.ldb + n0) * 2);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc_u((const char*)p.B + (k0 * p.ldb + n0) * 2);
                 static_for<B0, B1>([&](auto J) __attribute__((always_inline)) {
                     constexpr int j = J;
                     const int q = j * C::NL + wave;
@@ -1241,31 +1257,21 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
     epi(ml, acc);
 }
 
-// Calls f(variant) with the loop variant this call needs, as a constant.
-// ALL = false compiles only the main variant (plain GEMM K, whole filter taps
-// per K tile); the host never sends such a kernel a call that needs another.
-template <class C, bool ALL, class F>
-__device__ __forceinline__ void with_variant(const Params p, F&& f) {
-    if constexpr (!ALL) {
-        f(std::integral_constant<int, C::GATHER_A ? UNIFORM_TAP : PLAIN>{});
-    } else if constexpr (C::GATHER_A) {
-        // channels are a multiple of 8, so K never is ragged
-        if (!p.conv_masks)
-            f(std::integral_constant<int, CONV_GENERIC>{});
-        else if (p.conv_uniform)
-            f(std::integral_constant<int, UNIFORM_TAP>{});
-        else
-            f(std::integral_constant<int, PLAIN>{});
-    } else if constexpr (C::WGRAD) {
-        // neither operand is K-contiguous: a K tail is masked by whole LDS rows
-        f(std::integral_constant<int, PLAIN>{});
-    } else {
-        if (p.k_ragged8)
-            f(std::integral_constant<int, RAGGED>{});
-        else
-            f(std::integral_constant<int, PLAIN>{});
-    }
+// The loop variants an operation has, and the one every build includes.  Each
+// variant is its own kernel: the host picks the one a call needs (a unit
+// stride and small filter give masks, channel counts that are multiples of the
+// K tile give whole taps per tile, K % 8 decides the ragged GEMM loop), so no
+// loop carries a branch between its MFMAs and each loop gets its own register
+// allocation (loops compiled into one kernel share one, and the largest ring's
+// loops then spill).
+template <class C, int V>
+constexpr bool variant_applies() {
+    if constexpr (C::GATHER_A) return V == PLAIN || V == UNIFORM_TAP || V == CONV_GENERIC;
+    else if constexpr (C::WGRAD) return V == PLAIN;
+    else return V == PLAIN || V == RAGGED;
 }
+template <class C>
+constexpr int main_variant() { return C::GATHER_A ? UNIFORM_TAP : PLAIN; }
 
 // End (exclusive) of stream-K workgroup g's run of K units.
 __device__ __forceinline__ int64_t sk_end(int64_t total, int G, int g) { return total * (g + 1) / G; }
@@ -1284,50 +1290,33 @@ struct WorkItem {
     int64_t tile_start;  // ROLE_OWN: the tile's first K unit in the concatenated stream-K range
 };
 
-// The workgroup's schedule, one item at a time.
-//  * Data-parallel grid (sk_grid == 0): one item, tile blockIdx % T (in the
-//    XCD-aware order of tile_coords), K split blockIdx / T.
-//  * Stream-K (sk_grid = G): workgroup g first computes whole tiles g, g+G,
-//    ... below sk_dp_tiles (data-parallel rounds in the same XCD order), then
-//    takes the K units [b, e) of the remaining tiles' concatenated K ranges and
-//    walks them backwards, one tile segment at a time, so that it first
-//    finishes the segment it shares with higher workgroups (publishing a
-//    partial) and last the segment whose tile it owns (collecting the partials
-//    of lower workgroups, which published theirs first).  An owner therefore
-//    only waits on workgroups dispatched no later than itself.
+// The stream-K workgroup's schedule, one item at a time.  Workgroup g first
+// computes whole tiles g, g+G, ... below sk_dp_tiles (data-parallel rounds in
+// the XCD order of tile_coords), then takes the K units [b, e) of the
+// remaining tiles' concatenated K ranges and walks them backwards, one tile
+// segment at a time, so that it first finishes the segment it shares with
+// higher workgroups (publishing a partial) and last the segment whose tile it
+// owns (collecting the partials of lower workgroups, which published theirs
+// first).  An owner therefore only waits on workgroups dispatched no later
+// than itself.
 struct Schedule {
     int G, g;
     int64_t T, Tdp, UT, total, b, hi, blk;
-    bool done;
 
     __device__ __forceinline__ explicit Schedule(const Params& p) {
         G = p.sk_grid;
         g = (int)blockIdx.x;
         T = (int64_t)p.tiles_m * p.tiles_n;
-        done = false;
-        if (G > 0) {
-            Tdp = p.sk_dp_tiles;
-            UT = p.sk_units;
-            total = (T - Tdp) * UT;
-            b = total * g / G;
-            hi = sk_end(total, G, g);
-            blk = g;
-        }
+        Tdp = p.sk_dp_tiles;
+        UT = p.sk_units;
+        total = (T - Tdp) * UT;
+        b = total * g / G;
+        hi = sk_end(total, G, g);
+        blk = g;
     }
 
     template <int UNIT>
     __device__ __forceinline__ bool next(const Params& p, WorkItem& it) {
-        if (G <= 0) {
-            if (done) return false;
-            done = true;
-            it.split = (int)(blockIdx.x / T);
-            tile_coords((int)(blockIdx.x - (int64_t)it.split * T), p.tiles_m, p.tiles_n, p.group_m, it.tm, it.tn);
-            it.kbase = (int64_t)it.split * p.k_per_split;
-            it.kend = it.kbase + p.k_per_split < p.K ? it.kbase + p.k_per_split : p.K;
-            it.role = p.k_splits > 1 ? ROLE_SPLIT : ROLE_STORE;
-            it.tile_start = 0;
-            return true;
-        }
         if (blk < Tdp) {
             tile_coords((int)blk, p.tiles_m, p.tiles_n, p.group_m, it.tm, it.tn);
             it.kbase = 0;
@@ -1396,20 +1385,39 @@ __device__ __forceinline__ void finish_item(ML& ml, typename C::Acc (&acc)[C::FM
     }
 }
 
-// The kernel: the workgroup's work items one after another.  The K loop is
-// instantiated once per loop variant (and per loading / compute-only wave),
-// whatever the schedule.
-template <class C, bool ALL>
+// The data-parallel kernel of loop variant V: one workgroup per output tile
+// (tile blockIdx % T in the XCD-aware order of tile_coords) and K split
+// blockIdx / T.  It keeps no schedule state across its K loop: the loops of
+// the largest tiles sit at the register limit, and any state kept alive around
+// them spills inside.
+template <class C, int V>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
+    static_assert(variant_applies<C, V>(), "loop variant of another operation");
+    const int T = p.tiles_m * p.tiles_n;
+    const int split = (int)blockIdx.x / T;
+    int tm, tn;
+    tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int64_t kbase = (int64_t)split * p.k_per_split;
+    const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
+    run_tile<C, V>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
+        if (p.k_splits > 1)
+            ml.store(acc, p.ws + split * p.ws_stride, p.ldws, OUT_F32, true);
+        else
+            store_tile<C>(ml, acc, p.C, p.ldc, p.out_kind, p.vec_ok);
+    });
+}
+
+// The stream-K kernel of loop variant V: the workgroup's work items one after
+// another.
+template <class C, int V>
+__global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const Params p) {
+    static_assert(variant_applies<C, V>(), "loop variant of another operation");
     constexpr int UNIT = C::P * C::BK;  // stream-K unit: K elements of one ring period
     Schedule sch(p);
     WorkItem it;
     while (sch.template next<UNIT>(p, it)) {
-        with_variant<C, ALL>(p, [&](auto v) __attribute__((always_inline)) {
-            run_tile<C, decltype(v)::value>(p, it.tm, it.tn, it.kbase, it.kend,
-                                            [&](auto& ml, auto& acc) __attribute__((always_inline)) {
-                                                finish_item<C>(ml, acc, p, it, sch);
-                                            });
+        run_tile<C, V>(p, it.tm, it.tn, it.kbase, it.kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {
+            finish_item<C>(ml, acc, p, it, sch);
         });
         __syncthreads();  // every wave is past this item's LDS before the next prologue
     }

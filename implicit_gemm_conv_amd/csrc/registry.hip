@@ -8,10 +8,10 @@ static const igc_tune_t kTunes[] = {
     IGC_FOR_EACH_TILE(IGC_TUNE_ENTRY)
 #undef IGC_TUNE_ENTRY
 };
-static const bool kFull[] = {
-#define IGC_FULL_ENTRY(BM, BN, BK, D, W, MI, H, L, SY, F) F != 0,
-    IGC_FOR_EACH_TILE(IGC_FULL_ENTRY)
-#undef IGC_FULL_ENTRY
+static const int kScope[] = {
+#define IGC_SCOPE_ENTRY(BM, BN, BK, D, W, MI, H, L, SY, F) F,
+    IGC_FOR_EACH_TILE(IGC_SCOPE_ENTRY)
+#undef IGC_SCOPE_ENTRY
 };
 
 // Tables registered by the instance objects while the library loads (static
@@ -33,7 +33,7 @@ int num_tunes() { return (int)(sizeof(kTunes) / sizeof(kTunes[0])); }
 
 igc_tune_t tune_at(int i) { return kTunes[i]; }
 
-bool tune_is_full(int i) { return kFull[i]; }
+int tune_scope(int i) { return kScope[i]; }
 
 const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_kc, int op) {
     const int mfma = q.mfma == 0 ? 32 : q.mfma;
@@ -52,37 +52,36 @@ const Instance* find_instance(const igc_tune_t& q, bool fp16, bool a_kc, bool b_
 
 igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op) {
     constexpr int64_t kCUs = 256;
-    igc_tune_t t = {256, 256, 32, 4, 8, 16, 0, 4, 1, 0, 0, 0};
-    // Enough 256x256 tiles for every CU: the largest tile (least global and LDS
-    // traffic per flop), 8 waves, 32-deep K tiles in a 4-stage ring, 16x16x32
-    // MFMAs (which hold a higher clock than 32x32x16 under load) and loads
-    // issued by one wave per SIMD: measured fastest, by a small margin, for
-    // both the GEMM and the convolution once the output tile is stored
-    // through LDS.
+    // 256 x 256 output tiles, 8 waves, 16x16x32 MFMAs, loads issued by one
+    // wave per SIMD.  The GEMM and the forward convolution use 64-deep K tiles
+    // in a ring of two and a half stages (160 KB); the data gradient, whose
+    // gathered A and row-major filter rows need more per-lane load state, uses
+    // 32-deep K tiles in four stages (the 64-deep ring's loading waves spill).
+    const igc_tune_t big = op == IGC_OP_CONV_DGRAD ? igc_tune_t{256, 256, 32, 4, 8, 16, 0, 4, 1, 0, 0, 0}
+                                          : igc_tune_t{256, 256, 64, 2, 8, 16, 1, 4, 1, 0, 0, 0};
+    // 128 x 128 tiles, 8 waves, 16x16x32 MFMAs, 64-deep K tiles in four stages.
+    igc_tune_t small = {128, 128, 64, 4, 8, 16, 0, 4, 1, 0, 0, 0};
+    // Whole rounds of tiles over the CUs decide: a round of 128 x 128 tiles
+    // took 0.31 of a round of 256 x 256 tiles on the measured workloads (a
+    // quarter of the work, at lower efficiency), so the larger tile wins unless
+    // it leaves most of its last round idle or pads the output heavily.
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    // 256x256 tiles unless they pad the output by more than a third more than
-    // 128x128 tiles do (a 64-wide N, say) while 128x128 still fills the CUs
-    const bool wasteful = t256 * 65536 * 3 > t128 * 16384 * 4 && t128 >= kCUs;
-    if (t256 >= kCUs && !wasteful) {
-        // A last round of tiles that leaves CUs idle (for the 3x3 convolution,
-        // 392 tiles = 1.53 rounds) is spread over every CU: whole tiles in
-        // data-parallel rounds, then the remaining tiles' K ranges cut into
-        // equal runs (stream-K), when the K range is deep enough to split.
-        const int64_t rem = t256 % kCUs;
-        if (rem != 0 && rem * 4 < kCUs * 3 && K >= 1024) {
-            t.stream_k = (int)kCUs;
-            t.sk_hybrid = 1;
-        }
-        (void)op;
-        return t;
+    const int64_t r256 = (t256 + kCUs - 1) / kCUs, r128 = (t128 + kCUs - 1) / kCUs;
+    if (t256 > 0 && r256 * 100 <= r128 * 31) return big;
+    // Small tiles.  When even they leave CUs idle and K is deep (at least 2048
+    // per CU's share), the K work is spread over every CU: a 2-way split when
+    // the tiles fill exactly half the CUs (each workgroup one half of a tile,
+    // summed by the reduction kernel), stream-K otherwise (measured: 2-way
+    // split 79 us vs stream-K 82-87 us on 2048 x 1024 x 16384; stream-K 176 us
+    // vs a 4-way split 194 us on 1000 x 1000 x 65536).
+    if (t128 > 0 && t128 < kCUs && K / 2048 >= 2) {
+        if (t128 * 2 == kCUs)
+            small.k_splits = 2;
+        else
+            small.stream_k = (int)kCUs;
     }
-    // Otherwise 128x128 tiles; when even those leave CUs idle and K is deep
-    // (at least 2048 per CU's share), stream-K over every CU balances the K
-    // work; shallow K runs one tile per workgroup.
-    t = igc_tune_t{128, 128, 64, 4, 4, 32, 0, 4, 1, 0, 0, 0};
-    if (t128 > 0 && t128 < kCUs && K / 2048 >= 2) t.stream_k = (int)kCUs;
-    return t;
+    return small;
 }
 
 }  // namespace igc

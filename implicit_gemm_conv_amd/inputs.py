@@ -49,6 +49,13 @@ WORKLOADS = {
     "conv_bf16_n16_27x27_c256_k256_3x3": dict(kind="conv", N=16, H=27, W=27, C=256, K=256, R=3, S=3, sh=1, sw=1,
                                               ph=1, pw=1, dh=1, dw=1, dtype="bf16", out="bf16",
                                               a_dist=("normal", 1.0), b_dist=("normal", 0.02), seed=9),
+    # the gradients of the 3x3 convolution on the same mainloop: dx from (dy, w), dw from (x, dy)
+    "dgrad_bf16_n32_56x56_c256_k256_3x3": dict(kind="dgrad", N=32, H=56, W=56, C=256, K=256, R=3, S=3, sh=1, sw=1,
+                                               ph=1, pw=1, dh=1, dw=1, dtype="bf16", out="bf16",
+                                               a_dist=("normal", 1.0), b_dist=("normal", 0.02), seed=10),
+    "wgrad_bf16_n32_56x56_c256_k256_3x3": dict(kind="wgrad", N=32, H=56, W=56, C=256, K=256, R=3, S=3, sh=1, sw=1,
+                                               ph=1, pw=1, dh=1, dw=1, dtype="bf16", out="f32",
+                                               a_dist=("normal", 1.0), b_dist=("normal", 1.0), seed=11),
 }
 
 _TORCH = {"bf16": torch.bfloat16, "fp16": torch.float16}
@@ -95,10 +102,29 @@ def conv_operands(N, H, W, C, K, R, S, dtype="bf16", a_dist=("normal", 1.0), b_d
     return x, w
 
 
+def conv_out_hw(cfg):
+    """(P, Q) of a convolution workload."""
+    return ((cfg["H"] + 2 * cfg["ph"] - cfg["dh"] * (cfg["R"] - 1) - 1) // cfg["sh"] + 1,
+            (cfg["W"] + 2 * cfg["pw"] - cfg["dw"] * (cfg["S"] - 1) - 1) // cfg["sw"] + 1)
+
+
 def workload_operands(name):
+    """gemm: (A, lda, B, ldb); conv: (x NHWC, w KRSC); dgrad: (dy NPQK, w KRSC); wgrad: (x NHWC, dy NPQK).  The
+    first operand is drawn before the second."""
     cfg = WORKLOADS[name]
     if cfg["kind"] == "gemm":
         return gemm_operands(cfg["M"], cfg["N"], cfg["K"], cfg["la"], cfg["lb"], dtype=cfg["dtype"],
                              a_dist=cfg["a_dist"], b_dist=cfg["b_dist"], seed=cfg["seed"])
-    return conv_operands(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], dtype=cfg["dtype"],
-                         a_dist=cfg["a_dist"], b_dist=cfg["b_dist"], seed=cfg["seed"])
+    if cfg["kind"] == "conv":
+        return conv_operands(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], dtype=cfg["dtype"],
+                             a_dist=cfg["a_dist"], b_dist=cfg["b_dist"], seed=cfg["seed"])
+    P, Q = conv_out_hw(cfg)
+    N, H, W, C, K, R, S = (cfg[k] for k in ("N", "H", "W", "C", "K", "R", "S"))
+    gen = torch.Generator().manual_seed(cfg["seed"])
+    if cfg["kind"] == "dgrad":
+        dy = draw(N * P * Q * K, cfg["a_dist"], cfg["dtype"], gen).reshape(N, P, Q, K)
+        w = draw(K * R * S * C, cfg["b_dist"], cfg["dtype"], gen).reshape(K, R, S, C)
+        return dy, w
+    x = draw(N * H * W * C, cfg["a_dist"], cfg["dtype"], gen).reshape(N, H, W, C)
+    dy = draw(N * P * Q * K, cfg["b_dist"], cfg["dtype"], gen).reshape(N, P, Q, K)
+    return x, dy

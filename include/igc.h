@@ -105,9 +105,9 @@ typedef enum { IGC_OP_GEMM = 0, IGC_OP_CONV_FPROP = 1, IGC_OP_CONV_DGRAD = 2, IG
  * k_splits > 1 together with stream_k > 0, stream_k < 0, or sk_hybrid without
  * stream_k is IGC_ERR_INVALID_VALUE.  Only compiled (bm, bn, bk, pipe_depth,
  * waves, mfma, half_stage, loader_waves, ring_sync) combinations are accepted
- * (igc_tune_count / igc_tune_get list them, igc_tune_full says which are
- * built for every input type, layout and operation); NULL selects the
- * built-in choice for the shape (igc_default_tune). */
+ * (igc_tune_count / igc_tune_get list them, igc_tune_scope says what each
+ * is built for); NULL selects the built-in choice for the shape
+ * (igc_default_tune). */
 typedef struct {
     int bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves, k_splits, stream_k, ring_sync, sk_hybrid;
 } igc_tune_t;
@@ -254,9 +254,9 @@ igc_status_t conv2d_nhwc_wgrad_implicit_gemm_fp16_ex(int N, int H, int W, int C,
 
 /* gemm_bf16 for callers that cannot allocate (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the built-in
- * schedule, with its workspace (stream-K partial tiles and flags) in a
- * library-owned device array of 64 MiB + 4 KiB that each GPU holds until the
- * process ends.  The call allocates nothing and gives the same bits as
+ * schedule, with its workspace (K-split or stream-K partial tiles and flags)
+ * in a library-owned device array of 16 MiB + 4 KiB that each GPU holds until
+ * the process ends.  The call allocates nothing and gives the same bits as
  * gemm_bf16.  Calls that overlap on one GPU share the array and race: order
  * them (one stream).  A shape whose schedule needs more than the array holds is
  * IGC_ERR_UNSUPPORTED (the built-in choice never does); IGC_ERR_HIP if the
@@ -279,12 +279,16 @@ int igc_tune_supported(const igc_tune_t *tune);
  * M x N x K when no tune is given; 1 on success. */
 int igc_default_tune(igc_op_t op, int64_t M, int64_t N, int64_t K, igc_tune_t *out);
 
-/* Number of compiled configurations; igc_tune_get(i, &t) fills t for i in [0, count);
- * igc_tune_full(i) is 1 if configuration i is built for every input type, operand layout and operation,
- * 0 if only for the bf16 GEMM with row-major A and the bf16 forward convolution. */
+/* Number of compiled configurations; igc_tune_get(i, &t) fills t for i in [0, count).
+ * igc_tune_scope(i) is a bit mask of what configuration i is built for: IGC_SCOPE_ALL (every input type,
+ * operand layout, operation and loop variant; without it only the bf16 and fp16 GEMM with row-major A and
+ * K % 8 == 0, and the bf16 forward convolution with whole filter taps per K tile and filters of at most
+ * 16 x 16 -- other calls are IGC_ERR_UNSUPPORTED) and IGC_SCOPE_STREAM_K (stream-K schedules; without it
+ * a tune with stream_k > 0 is IGC_ERR_UNSUPPORTED); 0 for an index out of range. */
+enum { IGC_SCOPE_ALL = 1, IGC_SCOPE_STREAM_K = 2 };
 int igc_tune_count(void);
 int igc_tune_get(int i, igc_tune_t *out);
-int igc_tune_full(int i);
+int igc_tune_scope(int i);
 
 /* LDS bytes one workgroup of the given configuration uses (0 if not compiled). */
 int64_t igc_tune_lds_bytes(const igc_tune_t *tune);

@@ -81,6 +81,7 @@ FAKE = 1 << 20  # a 16-byte aligned address that is never dereferenced (validati
     (dict(tune=(256, 256, 32, 4, 8, 16, 0, 4, 1, 256), ws=FAKE + 16, ws_bytes=1 << 30),
      igc.IGC_ERR_INVALID_VALUE),                                                    # workspace not 256-byte aligned
     (dict(K=40, lda=40, tune=(256, 256, 32, 2, 8, 32, 0, 4)), igc.IGC_ERR_UNSUPPORTED),  # study tile: no ragged K
+    (dict(tune=(256, 256, 32, 2, 8, 32, 0, 4, 1, 16)), igc.IGC_ERR_UNSUPPORTED),  # no stream-K kernel built
     (dict(M=0), igc.IGC_OK),                            # empty output: no-op
     (dict(N=0), igc.IGC_OK),
 ])
@@ -188,7 +189,10 @@ def test_tune_table_fits_lds():
     """Every compiled ring fits the 160 KB of LDS of one CU (a stage costs (BM+BN)*BK*2 bytes)."""
     tunes = igc.tunes()
     assert (256, 256, 32, 4, 8, 16, 0, 4, 0) in tunes and (256, 256, 64, 2, 8, 16, 1, 4, 0) in tunes
-    assert set(igc.tunes(full_only=True)) >= {(256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)}
+    # the built-in choices are built for everything
+    assert set(igc.tunes(igc.SCOPE_ALL | igc.SCOPE_STREAM_K)) >= {(256, 256, 64, 2, 8, 16, 1, 4, 0),
+                                                                  (256, 256, 32, 4, 8, 16, 0, 4, 0),
+                                                                  (128, 128, 64, 4, 8, 16, 0, 4, 0)}
     for (bm, bn, bk, d, w, mi, h, lw, sy) in tunes:
         assert 1 <= lw <= w and w % lw == 0
         lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw, sy))
@@ -206,23 +210,27 @@ def test_tune_table_fits_lds():
     assert igc.igc_tune_supported((256, 256, 32, 5, 8, 16, 0, 4)) == 0  # 5 stages x 1 k-step: odd fragment parity
 
 
-BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)
+T25 = (256, 256, 64, 2, 8, 16, 1, 4, 0)   # 256 x 256 x 64, two and a half stages: GEMM and forward convolution
+BIG = (256, 256, 32, 4, 8, 16, 0, 4, 0)   # 256 x 256 x 32, four stages: data gradient
+S8 = (128, 128, 64, 4, 8, 16, 0, 4, 0)    # 128 x 128 x 64, 8 waves: small grids
 
 
 @pytest.mark.parametrize("shape,op,expect", [
-    ((8192, 8192, 8192), igc.OP_GEMM, (BIG, 1, 0, 0)),              # 1024 tiles of 256x256: data-parallel
-    ((100352, 256, 2304), igc.OP_CONV_FPROP, (BIG, 1, 256, 1)),     # the 3x3 conv's GEMM view: 392 tiles = 1.53
-    ((100352, 256, 2304), igc.OP_CONV_DGRAD, (BIG, 1, 256, 1)),     # rounds, so 256 whole tiles then stream-K
-    ((100352, 256, 2304), igc.OP_GEMM, (BIG, 1, 256, 1)),
-    ((100352, 256, 512), igc.OP_GEMM, (BIG, 1, 0, 0)),              # too little K to split the last round
-    ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (BIG, 1, 0, 0)),      # last round 99% full: data-parallel
-    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (SMALL, 1, 256, 0)),   # the conv's filter gradient: 36 tiles, deep K
-    ((2048, 1024, 16384), igc.OP_GEMM, (SMALL, 1, 256, 0)),         # 128 tiles of 128x128: stream-K
-    ((1000, 1000, 65536), igc.OP_GEMM, (SMALL, 1, 256, 0)),         # 64 tiles
-    ((1000, 1000, 3000), igc.OP_GEMM, (SMALL, 1, 0, 0)),            # too little K to share
-    ((100352, 64, 256), igc.OP_CONV_FPROP, (SMALL, 1, 0, 0)),       # 1x1 conv with 64 outputs: 128-wide tiles
-    ((128, 96, 200), igc.OP_GEMM, (SMALL, 1, 0, 0)),
-    ((0, 5, 7), igc.OP_GEMM, (SMALL, 1, 0, 0)),
+    ((8192, 8192, 8192), igc.OP_GEMM, (T25, 1, 0, 0)),               # 1024 tiles of 256x256: data-parallel
+    ((100352, 256, 2304), igc.OP_CONV_FPROP, (T25, 1, 0, 0)),        # the 3x3 conv's GEMM view: 392 tiles
+    ((100352, 256, 2304), igc.OP_CONV_DGRAD, (BIG, 1, 0, 0)),        # its data gradient: the 32-deep ring
+    ((100352, 256, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
+    ((25088, 512, 2304), igc.OP_CONV_FPROP, (T25, 1, 0, 0)),         # stride-2 conv: 196 big tiles (1 round) beat
+                                                                     # 784 small ones (4 rounds)
+    ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
+    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (S8, 1, 256, 0)),       # the conv's filter gradient: 36 tiles, deep K
+    ((2048, 1024, 16384), igc.OP_GEMM, (S8, 2, 0, 0)),               # 128 tiles of 128x128 = half the CUs: 2-way split
+    ((1000, 1000, 65536), igc.OP_GEMM, (S8, 1, 256, 0)),             # 64 tiles: stream-K
+    ((1000, 1000, 3000), igc.OP_GEMM, (S8, 1, 0, 0)),                # too little K to share
+    ((100352, 64, 256), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),           # 1x1 conv with 64 outputs: 128-wide tiles
+    ((11664, 256, 2304), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),          # 27x27 images: 46 big tiles vs 184 small
+    ((128, 96, 200), igc.OP_GEMM, (S8, 1, 0, 0)),
+    ((0, 5, 7), igc.OP_GEMM, (S8, 1, 0, 0)),
 ])
 def test_default_tune(shape, op, expect):
     t = igc.igc_default_tune(*shape, op=op)
@@ -235,12 +243,15 @@ def test_workspace_bytes():
     to 256 bytes), or S fp32 partial outputs (rows rounded to 4 floats) for a K split; nothing otherwise."""
     ws = igc.igc_workspace_bytes
     assert ws(igc.OP_GEMM, 8192, 8192, 8192) == 0
-    assert ws(igc.OP_GEMM, 2048, 1024, 16384) == 256 * 128 * 128 * 4 + 1024
-    assert ws(igc.OP_CONV_FPROP, 100352, 256, 2304) == 256 * 256 * 256 * 4 + 1024
+    assert ws(igc.OP_CONV_FPROP, 100352, 256, 2304) == 0
+    assert ws(igc.OP_GEMM, 2048, 1024, 16384) == 2 * 2048 * 1024 * 4
+    assert ws(igc.OP_GEMM, 1000, 1000, 65536) == 256 * 128 * 128 * 4 + 1024
     assert ws(igc.OP_GEMM, 1000, 1000, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
     assert ws(igc.OP_GEMM, 1000, 998, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
     # stream-K with fewer K units than workgroups: G clamps to the units (2 tiles x 1 unit of 256)
     assert ws(igc.OP_GEMM, 256, 128, 200, (128, 128, 64, 4, 4, 32, 0, 4, 1, 100)) == 2 * 128 * 128 * 4 + 256
+    # hybrid: 392 tiles of 256x256 over 256 workgroups, 256 whole tiles first, then stream-K
+    assert ws(igc.OP_GEMM, 100352, 256, 2304, igc.tune(BIG, stream_k=256, sk_hybrid=1)) == 256 * 256 * 256 * 4 + 1024
     # hybrid whose tiles fill whole rounds: no tile is split, no workspace
     assert ws(igc.OP_GEMM, 256 * 16, 256 * 16, 4096, (256, 256, 32, 4, 8, 16, 0, 4, 1, 256, 0, 1)) == 0
     assert ws(igc.OP_GEMM, 0, 5, 7) == 0

@@ -19,7 +19,8 @@ from gpu_util import assert_close, round_to, run_conv, say
 
 pytestmark = pytest.mark.gpu
 
-BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)
+# the configurations built for every operation
+T25, BIG, S8 = (256, 256, 64, 2, 8, 16, 1, 4, 0), (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 8, 16, 0, 4, 0)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -61,7 +62,7 @@ def test_dgrad(case):
         w = inputs.draw(K * R * S * C, ("normal", 0.1), dtype, gen).reshape(K, R, S, C)
         ref, Sabs = oracle.conv2d_dgrad_nhwc(N, H, W, C, K, R, S, dy, w, oracle.FP16 if dtype == "fp16" else
                                              oracle.BF16, **geo)
-        for tune in (None, SMALL, BIG):
+        for tune in (None, S8, BIG, T25):
             say(f"dgrad {case} {dtype}->{out} tune={tune}")
             y, _ = run_conv(N, H, W, C, K, R, S, dy, w, out=out, dtype=dtype, tune=tune, op="dgrad", **geo)
             assert_close(y, ref, Sabs, out, f"dgrad {case} {dtype}->{out} tune={tune}")
@@ -78,7 +79,7 @@ def test_wgrad(case):
         dy = inputs.draw(N * P * Q * K, ("normal", 1.0), dtype, gen).reshape(N, P, Q, K)
         ref, Sabs = oracle.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, x, dy, oracle.FP16 if dtype == "fp16" else
                                              oracle.BF16, **geo)
-        for tune in (None, SMALL, BIG, igc.tune(SMALL, k_splits=3), igc.tune(BIG, stream_k=5)):
+        for tune in (None, S8, BIG, T25, igc.tune(S8, k_splits=3), igc.tune(BIG, stream_k=5)):
             say(f"wgrad {case} {dtype}->{out} tune={tune}")
             y, _ = run_conv(N, H, W, C, K, R, S, x, dy, out=out, dtype=dtype, tune=tune, op="wgrad", **geo)
             assert_close(y, ref, Sabs, out, f"wgrad {case} {dtype}->{out} tune={tune}")
@@ -102,7 +103,7 @@ def test_grads_exact_integers(op, out):
     else:
         ref, _ = oracle.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, x, dy, oracle.BF16, **geo)
         args = (x, dy)
-    for tune in (None, SMALL, BIG, igc.tune(BIG, k_splits=2), igc.tune(SMALL, stream_k=7)):
+    for tune in (None, S8, BIG, T25, igc.tune(BIG, k_splits=2), igc.tune(S8, stream_k=7)):
         say(f"exact {op} -> {out} tune={tune}")
         y, _ = run_conv(N, H, W, C, K, R, S, *args, out=out, tune=tune, op=op, **geo)
         bad = np.count_nonzero(y != round_to(ref, out))
@@ -118,19 +119,14 @@ def test_dgrad_k_zero_writes_zeros():
     assert np.all(y == 0)
 
 
-NAME = "conv_bf16_n32_56x56_c256_k256_3x3"
-
-
 def test_workload_dgrad_sampled():
     """The 3x3 workload's data gradient at full size (N=32, 56x56, C=K=256) with the built-in schedule: every
-    channel of the corner and edge pixels of the first and last image, and 200k seeded samples."""
-    cfg = inputs.WORKLOADS[NAME]
+    channel of the corner and edge pixels of the first and last image, and 200k seeded samples, bf16 and fp32
+    output."""
+    cfg = inputs.WORKLOADS["dgrad_bf16_n32_56x56_c256_k256_3x3"]
     N, H, W, C, K, R, S = (cfg[k] for k in ("N", "H", "W", "C", "K", "R", "S"))
     geo = dict(sh=cfg["sh"], sw=cfg["sw"], ph=cfg["ph"], pw=cfg["pw"], dh=cfg["dh"], dw=cfg["dw"])
-    P, Q = out_hw(H, W, R, S, **geo)
-    gen = torch.Generator().manual_seed(cfg["seed"] + 100)
-    dy = inputs.draw(N * P * Q * K, ("normal", 1.0), "bf16", gen).reshape(N, P, Q, K)
-    _, w = inputs.workload_operands(NAME)
+    dy, w = inputs.workload_operands("dgrad_bf16_n32_56x56_c256_k256_3x3")
     for out in ("bf16", "f32"):
         say(f"workload dgrad -> {out}")
         y, _ = run_conv(N, H, W, C, K, R, S, dy, w, out=out, op="dgrad", **geo)
@@ -150,13 +146,10 @@ def test_workload_dgrad_sampled():
 def test_workload_wgrad_full():
     """The 3x3 workload's filter gradient at full size (K_gemm = N*P*Q = 100352), every output, fp32 output (the
     accumulator at the strict bound), with the built-in schedule."""
-    cfg = inputs.WORKLOADS[NAME]
+    cfg = inputs.WORKLOADS["wgrad_bf16_n32_56x56_c256_k256_3x3"]
     N, H, W, C, K, R, S = (cfg[k] for k in ("N", "H", "W", "C", "K", "R", "S"))
     geo = dict(sh=cfg["sh"], sw=cfg["sw"], ph=cfg["ph"], pw=cfg["pw"], dh=cfg["dh"], dw=cfg["dw"])
-    P, Q = out_hw(H, W, R, S, **geo)
-    x, _ = inputs.workload_operands(NAME)
-    gen = torch.Generator().manual_seed(cfg["seed"] + 100)
-    dy = inputs.draw(N * P * Q * K, ("normal", 1.0), "bf16", gen).reshape(N, P, Q, K)
+    x, dy = inputs.workload_operands("wgrad_bf16_n32_56x56_c256_k256_3x3")
     say("workload wgrad -> f32")
     y, _ = run_conv(N, H, W, C, K, R, S, x, dy, out="f32", op="wgrad", **geo)
     ref, Sabs = oracle.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, x, dy, oracle.BF16, **geo)

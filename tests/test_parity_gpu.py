@@ -23,15 +23,16 @@ pytestmark = pytest.mark.gpu
 NAN_BITS = {"bf16": 0x7FC0, "fp16": 0x7E00}
 
 
-def _compiled_tunes(full_only=False):
+def _compiled_tunes(scope=0):
     try:
-        return igc.tunes(full_only)
+        return igc.tunes(scope)
     except Exception:  # library not built: the GPU tests fail in the fixture below
         return [(256, 256, 32, 4, 8, 16, 0, 4, 0)]
 
 
 ALL_TUNES = _compiled_tunes()
-FULL_TUNES = set(_compiled_tunes(True))
+FULL_TUNES = set(_compiled_tunes(1))   # every type, layout and operation
+SK_TUNES = _compiled_tunes(2)          # stream-K kernel built
 BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)
 
 
@@ -245,7 +246,7 @@ def test_conv_split_k():
         assert_close(y, ref, Sabs, "bf16", f"conv split {S}")
 
 
-@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
+@pytest.mark.parametrize("tune", SK_TUNES, ids=[",".join(map(str, t)) for t in SK_TUNES])
 def test_stream_k(tune):
     """Stream-K over G persistent workgroups: runs that start and end inside tiles, runs inside one tile, more
     workgroups than K units (G clamps), ragged K, every layout and dtype."""
@@ -259,7 +260,7 @@ def test_stream_k(tune):
         gemm_case(M, N, K, la, lb, dtype=dtype, out=out, seed=400 + G, tune=igc.tune(tune, stream_k=G))
 
 
-@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
+@pytest.mark.parametrize("tune", SK_TUNES, ids=[",".join(map(str, t)) for t in SK_TUNES])
 def test_stream_k_hybrid(tune):
     """Whole tiles in data-parallel rounds of G, then stream-K over the tiles of the last, partial round: more
     tiles than workgroups, a tail shorter than G, tails with whole-tile runs, ragged K."""
@@ -309,7 +310,7 @@ def test_conv_stream_k():
     N, H, W, C, K = 2, 9, 7, 256, 136
     x, w = inputs.conv_operands(N, H, W, C, K, 3, 3, "bf16", seed=43)
     ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, 3, 3, x, w, oracle.BF16, ph=1, pw=1)
-    for tune in (igc.tune(BIG, stream_k=5), igc.tune((256, 256, 32, 4, 8, 32, 0, 4), stream_k=3),
+    for tune in (igc.tune(BIG, stream_k=5), igc.tune((128, 128, 64, 4, 8, 16, 0, 4), stream_k=3),
                  igc.tune(SMALL, stream_k=7), igc.tune((256, 256, 64, 2, 8, 16, 1, 4), stream_k=9),
                  igc.tune(BIG, stream_k=3, sk_hybrid=1)):
         say(f"conv stream-K {tune.astuple()} G={tune.stream_k} hybrid={tune.sk_hybrid}")
@@ -440,8 +441,9 @@ def test_conv_1x1_equals_gemm_on_gpu():
     assert_close(yg, ref, S, "f32", "1x1 as gemm")
 
 
-@pytest.mark.parametrize("stream_k", [0, 3])
-@pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
+@pytest.mark.parametrize("tune,stream_k", [(t, 0) for t in ALL_TUNES] + [(t, 3) for t in SK_TUNES],
+                         ids=[",".join(map(str, t)) + "-0" for t in ALL_TUNES] +
+                         [",".join(map(str, t)) + "-3" for t in SK_TUNES])
 def test_output_epilogue_exact(tune, stream_k):
     """Full tiles with a 16-bit output go through the LDS-staged epilogue (whole row segments per store), edge
     tiles and fp32 output store from the accumulators: every kind of tile in one call, with padding between N

@@ -64,7 +64,8 @@ def test_stream_k_wait_gives_up_loudly():
 
 
 @pytest.mark.parametrize("shape,tune", [
-    ((2048, 1024, 16384), None),                                  # built-in: 128 x 128 stream-K over 256
+    ((2048, 1024, 16384), None),                                  # built-in: 128 x 128, K split in two
+    ((1024, 1024, 8192), None),                                   # built-in: 128 x 128 stream-K over 256
     ((1000, 1000, 6144), igc.Tune(*SMALL[:8], 5, 0, 0, 0)),       # K split into 5
     ((1300, 1104, 2304), igc.Tune(*BIG[:8], 1, 8, 0, 1)),         # hybrid: 2 data-parallel rounds + tail
 ])
@@ -92,31 +93,35 @@ def test_caller_workspace(shape, tune):
 
 
 def test_conv_caller_workspace():
-    """The 3x3 workload's built-in hybrid schedule with a caller workspace equals the pool path bit for bit."""
+    """The 3x3 workload under the hybrid schedule (256 whole tiles in one data-parallel round, the other 136 split
+    by stream-K) with a caller workspace equals the pool path bit for bit and allocates nothing."""
     name = "conv_bf16_n32_56x56_c256_k256_3x3"
     c = inputs.WORKLOADS[name]
     x, w = inputs.workload_operands(name)
     dx, dw = to_dev(x), to_dev(w)
     M, Ng, Kg = igc.conv_gemm_view(igc.OP_CONV_FPROP, c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], 1, 1,
                                    1, 1)
-    need = igc.igc_workspace_bytes(igc.OP_CONV_FPROP, M, Ng, Kg)
+    tune = igc.tune(BIG, stream_k=256, sk_hybrid=1)
+    need = igc.igc_workspace_bytes(igc.OP_CONV_FPROP, M, Ng, Kg, tune)
     assert need > 0
     outs = []
     for ws in (None, torch.empty(need, dtype=torch.uint8, device="cuda")):
+        before = igc.igc_pool_allocations()
         y = torch.full((M * Ng,), float("nan"), dtype=torch.bfloat16, device="cuda")
         igc.check(igc.conv2d_nhwc_implicit_gemm_ex(c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], 1, 1, 1, 1,
-                                                   1, 1, dx, dw, y, igc.OUT_BF16, None, ws))
+                                                   1, 1, dx, dw, y, igc.OUT_BF16, tune, ws))
         synchronize()
+        assert (igc.igc_pool_allocations() == before) == (ws is not None)
         outs.append(y)
     assert torch.equal(outs[0], outs[1])
     assert not torch.isnan(outs[0].float()).any()
 
 
 def test_stream_k_graph_replay():
-    """A built-in stream-K call (2048 x 1024 x 8192: 128 tiles of 128 x 128 over 256 workgroups) captured in a
+    """A built-in stream-K call (1024 x 1024 x 8192: 64 tiles of 128 x 128 over 256 workgroups) captured in a
     HIP graph with a caller workspace, replayed with new inputs each time, eager work and synchronisation between
     replays: every replay equals the eager call on the same inputs bit for bit."""
-    M, N, K = 2048, 1024, 8192
+    M, N, K = 1024, 1024, 8192
     t = igc.igc_default_tune(M, N, K)
     assert t.stream_k > 0
     need = igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K)
