@@ -302,6 +302,7 @@ struct Cfg {
     // reads of it are done, and waves wait only on the counter they need.
     static constexpr int SYNC = SYNC_;
     static_assert(SYNC == 0 || SYNC == 1, "barrier ring or counter ring");
+    static_assert(SYNC == 0 || (U >= 6 && U % 2 == 0), "the counter ring runs whole stages refilled during compute");
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave sub-tile is whole MFMA blocks");
@@ -316,7 +317,8 @@ struct Cfg {
     static constexpr int SLOT_MAX = SLOT_A > SLOT_B ? SLOT_A : SLOT_B;
     template <int S>
     static constexpr int slot_bytes() { return U % 2 ? SLOT_MAX : (S % 2 ? SLOT_B : SLOT_A); }
-    static constexpr int LDS_BYTES = U % 2 ? U * SLOT_MAX : D * (SLOT_A + SLOT_B);
+    // the ring, plus the per-stage ready and free counters of SYNC 1
+    static constexpr int LDS_BYTES = (U % 2 ? U * SLOT_MAX : D * (SLOT_A + SLOT_B)) + (SYNC_ ? 8 * D_ : 0);
     static constexpr int LPT = TA::IPW + TB::IPW;     // loads per K tile per wave
     // the slot pattern repeats every P tiles; the K loop is unrolled by P
     static constexpr int P = Ring::period(U);
@@ -1096,6 +1098,65 @@ __device__ __forceinline__ void store_tile(ML& ml, const typename C::Acc (&acc)[
     ml.store(acc, dst, ldc, kind, vec_ok);
 }
 
+// Per-stage counters of the SYNC 1 ring: ready[s] at [s], free[s] at [D + s].
+// A stage is filled once per pass around the ring, so after pass n (tiles
+// n*D + s) ready[s] reaches NL*(n+1) (each loading wave adds one when its own
+// loads into the stage have landed) and free[s] reaches NW*(n+1) (each wave
+// adds one when its reads of the stage have drained).
+template <class C>
+__device__ __forceinline__ IGC_LDS int* stage_counters() {
+    __shared__ int ctr[2 * C::D];
+    return (IGC_LDS int*)ctr;
+}
+
+// The counter operations are written as single instruction sequences: a
+// C-level poll loop (and the lane-0 branch of the atomic) splits the K loop
+// into many basic blocks, and across them the compiler no longer keeps the
+// accumulators in place (it renames and copies them, and the compute-only
+// copy of the loop spills).
+
+// One wave adds one to a counter: lane 0 alone issues the LDS atomic.
+__device__ __forceinline__ void count_up(IGC_LDS int* c) {
+    uint64_t save;
+    uint32_t one;
+    asm volatile(
+        "s_mov_b64 %[save], exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "v_mov_b32 %[one], 1\n\t"
+        "ds_add_u32 %[a], %[one]\n\t"
+        "s_mov_b64 exec, %[save]"
+        : [save] "=&s"(save), [one] "=&v"(one)
+        : [a] "v"((uint32_t)(uintptr_t)c)
+        : "memory");
+}
+
+// Waits until *c >= target, polling with a short sleep between reads; the
+// read is waited for inside the same sequence.  Bounded: after `limit` polls
+// it gives up and returns true (a protocol mistake then shows as a wrong,
+// reported result rather than a hung GPU).
+__device__ __forceinline__ bool wait_count(IGC_LDS int* c, int target, int limit = 1 << 22) {
+    uint32_t v;
+    int seen, n;
+    asm volatile(
+        "s_mov_b32 %[n], %[lim]\n"
+        "1:\n\t"
+        "ds_read_b32 %[v], %[a]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_readfirstlane_b32 %[seen], %[v]\n\t"
+        "s_cmp_ge_i32 %[seen], %[t]\n\t"
+        "s_cbranch_scc1 2f\n\t"
+        "s_sub_u32 %[n], %[n], 1\n\t"
+        "s_cmp_eq_u32 %[n], 0\n\t"
+        "s_cbranch_scc1 2f\n\t"
+        "s_sleep 1\n\t"
+        "s_branch 1b\n"
+        "2:"
+        : [v] "=&v"(v), [seen] "=&s"(seen), [n] "=&s"(n)
+        : [a] "v"((uint32_t)(uintptr_t)c), [t] "s"(target), [lim] "s"(limit)
+        : "memory", "scc");
+    return seen < target;
+}
+
 // The K range [kbase, kend) of one output tile: setup, the K loop of variant
 // V, then epi(ml, acc) with the accumulators.
 template <class C, int V, bool LOADER, class Epi>
@@ -1147,6 +1208,19 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
         // slot s % U.  Prologue: units 0 .. U-3; during tile t the units
         // 2t+U-2 and 2t+U-1 (the slots of tile t-1, freed by the barrier that
         // made tile t ready) are refilled by loads spread over its k-steps.
+        // SYNC 1 replaces each barrier by the stage counters: every wave marks
+        // tile t's stage free and (loading waves) tile t+1's stage ready, then
+        // waits for t+1 to be ready; a loading wave waits for a stage to be
+        // free only before refilling it, so compute-only waves never wait for
+        // another wave's reads.
+        constexpr bool CTR = C::SYNC == 1;
+        IGC_LDS int* ctr = nullptr;  // (the counters take LDS only in SYNC 1 instances)
+        bool late = false;  // a counter wait gave up
+        if constexpr (CTR) ctr = stage_counters<C>();
+        if constexpr (CTR) {
+            if (threadIdx.x < 2 * D) ctr[threadIdx.x] = 0;
+            __syncthreads();  // counters are zero before anyone counts (the previous item is done with them)
+        }
         constexpr int WAITN = Ring::wait_loads(U, ML::template ipw<0>(), ML::template ipw<1>());
         static_for<0, U - 2>([&](auto S) __attribute__((always_inline)) {
             constexpr int s = S;
@@ -1154,7 +1228,14 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
         });
         wait_vmcnt<WAITN>();
         ml.fixup_ragged_k(0, slot_a<C, 0>(), slot_b<C, 0>());
-        ring_barrier();
+        if constexpr (CTR) {
+            wait_lgkmcnt0();
+            compiler_fence();
+            if constexpr (LOADER) count_up(ctr + 0);  // tile 0 ready (stage 0, pass 0)
+            late |= wait_count(ctr + 0, C::NL);
+        } else {
+            ring_barrier();
+        }
         ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
         for (int t0 = 0; t0 < KTp; t0 += P) {
             static_for<0, P>([&](auto UU) __attribute__((always_inline)) {
@@ -1167,6 +1248,12 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
                 IGC_LDS char* d1 = slot<C, Ring::slot_of(U, s1)>();
                 IGC_LDS char* d2 = slot<C, Ring::slot_of(U, s2)>();
                 constexpr int p0 = (u * KK) & 1;  // fragment set of this tile's k-step 0
+                if constexpr (CTR && LOADER) {
+                    // the refill goes into the stage of tile t-1 (pass (t-1)/D, P == D here): every
+                    // wave must be done reading it; nothing to wait for before tile 0
+                    constexpr int sf = (u + D - 1) % D;
+                    late |= wait_count(ctr + D + sf, C::NW * (t0 / D + (u >= 1 ? 1 : 0)));
+                }
                 // k-steps 0 .. KK-2: refill, read ahead, MFMA
                 static_for<0, KK - 1>([&](auto KI) __attribute__((always_inline)) {
                     constexpr int kk = KI;
@@ -1182,7 +1269,16 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
                 // ready(t+1) and free(t): the units newer than B(t+1) may stay in flight
                 wait_vmcnt<WAITN>();
                 ml.fixup_ragged_k(t + 1, slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>());
-                ring_barrier();
+                if constexpr (CTR) {
+                    wait_lgkmcnt0();  // this wave's reads of tile t have drained
+                    compiler_fence();
+                    constexpr int sr = (u + 1) % D;
+                    count_up(ctr + D + u);                    // tile t's stage free
+                    if constexpr (LOADER) count_up(ctr + sr);  // tile t+1's stage ready (own loads landed)
+                    late |= wait_count(ctr + sr, C::NL * (t0 / D + (u + 1 == D ? 1 : 0) + 1));
+                } else {
+                    ring_barrier();
+                }
                 ml.read_frags(slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
                 ML::mma(acc, fa[pl], fb[pl]);
                 interleave<NMF, DSR, 0>();
@@ -1190,6 +1286,10 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
             });
         }
         wait_vmcnt<0>();  // the padding tiles past the loop are still landing in free slots
+        if constexpr (CTR) {
+            if (late && (threadIdx.x & 63) == 0)
+                __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(p.err_word), 0, 0, 1 | 16);
+        }
     } else if constexpr (D >= 2) {
         // ---- two stages, refilled in one burst right after the barrier
         static_for<0, D>([&](auto S) __attribute__((always_inline)) {

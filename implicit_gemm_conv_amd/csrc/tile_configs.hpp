@@ -25,5 +25,9 @@
     X(256, 256, 32, 5, 8, 32, 0, 4, 0, 0)     \
     X(256, 256, 64, 2, 4, 32, 0, 0, 0, 0)     \
     X(256, 256, 32, 4, 8, 16, 0, 0, 0, 0)     \
+    X(256, 256, 32, 4, 8, 16, 0, 4, 1, 2)     \
+    X(128, 128, 64, 4, 8, 16, 0, 4, 1, 2)     \
+    X(256, 256, 32, 3, 8, 32, 0, 4, 1, 0)     \
+    X(256, 256, 32, 4, 8, 32, 0, 4, 1, 0)     \
     X(256, 256, 64, 1, 4, 32, 0, 0, 0, 0)     \
     X(256, 128, 64, 3, 4, 32, 0, 0, 0, 0)

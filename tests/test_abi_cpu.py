@@ -197,7 +197,8 @@ def test_tune_table_fits_lds():
         assert 1 <= lw <= w and w % lw == 0
         lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw, sy))
         U = 2 * d + h
-        assert lds == ((bm + bn) * bk * 2 * d if U % 2 == 0 else U * max(bm, bn) * bk * 2)
+        # the ring, plus 8 bytes per stage of ready/free counters in a counter ring
+        assert lds == ((bm + bn) * bk * 2 * d if U % 2 == 0 else U * max(bm, bn) * bk * 2) + (8 * d if sy else 0)
         assert lds <= 160 * 1024
         assert igc.igc_tune_supported((bm, bn, bk, d, w, mi, h, lw, sy)) == 1
         if lw == w:  # loader_waves 0 means every wave
