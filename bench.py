@@ -122,51 +122,96 @@ def workload_cost(c):
     return conv_flops(c), 2 * ins + out_bytes * out
 
 
-def run_suite(reps, warmup):
-    """Every named workload with the library's built-in tile: mean and median launch time (HIP events on the
-    launch stream), TFLOP/s, and algorithmic HBM bandwidth."""
+def copy_calibration(mib):
+    """One plain device copy of `mib` MiB: a kernel of known traffic for scaling the hardware byte counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {n * 4} bytes read and written once")
+
+
+def workload_call(name, stream, tune=None):
+    """A closure that launches the named workload once on `stream` (tune None: the library's built-in choice),
+    with its operands resident in HBM; returns (call, tile actually used)."""
+    c = inputs.WORKLOADS[name]
+    out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[c["out"]]
+    if c["kind"] == "gemm":
+        A, lda, B, ldb = inputs.workload_operands(name)
+        dA = torch.from_numpy(A.view(np.int16)).cuda()
+        dB = torch.from_numpy(B.view(np.int16)).cuda()
+        dC = torch.empty((c["M"], c["N"]), dtype=out_dt, device="cuda")
+        fn = igc.gemm_fp16_ex if c["dtype"] == "fp16" else igc.gemm_bf16_ex
+        la, lb = (igc.ROW_MAJOR if c[k] == "row" else igc.COL_MAJOR for k in ("la", "lb"))
+        call = lambda: igc.check(fn(c["M"], c["N"], c["K"], dA, lda, la, dB, ldb, lb, dC, c["N"],
+                                    igc.OUT_CODES[c["out"]], tune, stream=stream))
+        used = igc.igc_default_tune(c["M"], c["N"], c["K"]) if tune is None else tune
+    else:
+        a0, a1 = inputs.workload_operands(name)
+        d0 = torch.from_numpy(a0.view(np.int16)).cuda()
+        d1 = torch.from_numpy(a1.view(np.int16)).cuda()
+        op, cfn = {"conv": (igc.OP_CONV_FPROP, igc.conv2d_nhwc_implicit_gemm_ex),
+                   "dgrad": (igc.OP_CONV_DGRAD, igc.conv2d_nhwc_dgrad_implicit_gemm_ex),
+                   "wgrad": (igc.OP_CONV_WGRAD, igc.conv2d_nhwc_wgrad_implicit_gemm_ex)}[c["kind"]]
+        view = igc.conv_gemm_view(op, c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"],
+                                  c["ph"], c["pw"], c["dh"], c["dw"])
+        dy = torch.empty((view[0] * view[1],), dtype=out_dt, device="cuda")
+        call = lambda: igc.check(cfn(
+            c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"], c["ph"], c["pw"], c["dh"],
+            c["dw"], d0, d1, dy, igc.OUT_CODES[c["out"]], tune, stream=stream))
+        used = igc.igc_default_tune(*view, op=op) if tune is None else tune
+    return call, used
+
+
+def time_launches(call, stream, reps, warmup):
+    """Launch times in ms (HIP events on the launch stream around each launch)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+
+
+def tile_string(t):
+    t = igc.tune(t) if not isinstance(t, igc.Tune) else t
+    return ",".join(map(str, t.astuple())) + (f" k_splits={t.k_splits}" if t.k_splits > 1 else "") + \
+        (f" stream_k={t.stream_k}" if t.stream_k > 0 else "")
+
+
+def run_suite(reps, warmup, only=None, cold=False):
+    """Every named workload (or those in `only`) with the library's built-in tile: mean and median launch time
+    (HIP events on the launch stream), TFLOP/s, and algorithmic HBM bandwidth.  `cold`: before every launch a
+    1 GiB buffer is rewritten on the same stream, which evicts the inputs from L2 and the 256 MB MALL, so the
+    launch reads them from HBM."""
     stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if cold else None
     rows = []
     for name, c in inputs.WORKLOADS.items():
-        out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[c["out"]]
-        if c["kind"] == "gemm":
-            A, lda, B, ldb = inputs.workload_operands(name)
-            dA = torch.from_numpy(A.view(np.int16)).cuda()
-            dB = torch.from_numpy(B.view(np.int16)).cuda()
-            dC = torch.empty((c["M"], c["N"]), dtype=out_dt, device="cuda")
-            fn = igc.gemm_fp16 if c["dtype"] == "fp16" else igc.gemm_bf16
-            la, lb = (igc.ROW_MAJOR if c[k] == "row" else igc.COL_MAJOR for k in ("la", "lb"))
-            call = lambda: igc.check(fn(c["M"], c["N"], c["K"], dA, lda, la, dB, ldb, lb, dC, c["N"],
-                                        igc.OUT_CODES[c["out"]], stream=stream))
-            t = igc.igc_default_tune(c["M"], c["N"], c["K"])
+        if only and name not in only:
+            continue
+        call, t = workload_call(name, stream)
+        if cold:
+            for _ in range(warmup):
+                call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for e0, e1 in ev:
+                flush.add_(1.0)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
         else:
-            a0, a1 = inputs.workload_operands(name)
-            P, Q = conv_geometry(c)
-            d0 = torch.from_numpy(a0.view(np.int16)).cuda()
-            d1 = torch.from_numpy(a1.view(np.int16)).cuda()
-            op, cfn = {"conv": (igc.OP_CONV_FPROP, igc.conv2d_nhwc_implicit_gemm),
-                       "dgrad": (igc.OP_CONV_DGRAD, igc.conv2d_nhwc_dgrad_implicit_gemm),
-                       "wgrad": (igc.OP_CONV_WGRAD, igc.conv2d_nhwc_wgrad_implicit_gemm)}[c["kind"]]
-            view = igc.conv_gemm_view(op, c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"],
-                                      c["ph"], c["pw"], c["dh"], c["dw"])
-            dy = torch.empty((view[0] * view[1],), dtype=out_dt, device="cuda")
-            call = lambda: igc.check(cfn(
-                c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], c["sh"], c["sw"], c["ph"], c["pw"], c["dh"],
-                c["dw"], d0, d1, dy, igc.OUT_CODES[c["out"]], stream=stream))
-            t = igc.igc_default_tune(*view, op=op)
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        ev[0].record(stream)
-        for i in range(reps):
-            call()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+            ms = time_launches(call, stream, reps, warmup)
         flops, nbytes = workload_cost(c)
-        tune = ",".join(map(str, t.astuple())) + (f" k_splits={t.k_splits}" if t.k_splits > 1 else "") + \
-            (f" stream_k={t.stream_k}" if t.stream_k > 0 else "")
+        tune = tile_string(t)
         row = {"workload": name, "us_mean": round(float(ms.mean()) * 1e3, 1),
                "us_median": round(float(np.median(ms)) * 1e3, 1),
                "tflops": round(flops / (ms.mean() * 1e-3) / 1e12, 1),
@@ -176,8 +221,123 @@ def run_suite(reps, warmup):
         rows.append(row)
         del call
         torch.cuda.empty_cache()
-    print(json.dumps({"suite": rows, "steps": reps, "warmup": warmup,
+    print(json.dumps({"suite": rows, "steps": reps, "warmup": warmup, "caches": "cold" if cold else "warm",
                       "note": "inputs resident in HBM; HIP events on the launch stream around each launch"}),
+          flush=True)
+
+
+def run_oracle_times(seconds=3.0):
+    """Wall time of the CPU oracle, as it is, on each named workload: a bounded slice (whole output rows of a GEMM,
+    whole images of a convolution, a seeded sample of a gradient), extrapolated per output element to the whole
+    workload, with the thread count it used; the small GEMM and the 3x3 convolution also on one thread."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    rows_out = []
+
+    def timed(f):
+        t0 = time.perf_counter()
+        f()
+        return time.perf_counter() - t0
+
+    def sized(run, n, limit):
+        """Grows the slice n until run(n) takes about `seconds` (or n reaches limit); returns (n, time)."""
+        t = timed(lambda: run(n))
+        while t < seconds / 8 and n < limit:
+            n = min(limit, n * 8)
+            t = timed(lambda: run(n))
+        if t < seconds and n < limit:
+            n = int(min(limit, n * seconds / max(t, 1e-6)))
+            t = timed(lambda: run(n))
+        if t < seconds / 8:  # the whole workload is quick: average over repeats
+            reps = int(seconds / max(t, 1e-6)) + 1
+            t = timed(lambda: [run(n) for _ in range(reps)]) / reps
+        return n, t
+
+    for name, c in inputs.WORKLOADS.items():
+        dt = oracle.FP16 if c["dtype"] == "fp16" else oracle.BF16
+        a0, *rest = inputs.workload_operands(name)
+        for th in ((threads, 1) if name in ("gemm_bf16_128x96x200", "conv_bf16_n32_56x56_c256_k256_3x3")
+                   else (threads,)):
+            if c["kind"] == "gemm":
+                A, lda, B, ldb = a0, rest[0], rest[1], rest[2]
+                M, N, K = c["M"], c["N"], c["K"]
+                la, lb = (oracle.ROW_MAJOR if c[k] == "row" else oracle.COL_MAJOR for k in ("la", "lb"))
+                # whole rows of the output when A is row-major, else the whole product
+                def run(r):
+                    if c["la"] == "row":
+                        return oracle.gemm(r, N, K, A[:r], lda, la, B, ldb, lb, dt, threads=th)
+                    return oracle.gemm(M, N, K, A, lda, la, B, ldb, lb, dt, threads=th)
+                r, t = sized(run, min(M, max(th, 8)), M if c["la"] == "row" else 0)
+                done, total, what = (r if c["la"] == "row" else M) * N, M * N, "outputs (whole rows)"
+            elif c["kind"] == "conv":
+                x, w = a0, rest[0]
+                geo = (c["sh"], c["sw"], c["ph"], c["pw"], c["dh"], c["dw"])
+                n = 1
+                t = timed(lambda: oracle.conv2d_nhwc(n, c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], x[:n], w, dt,
+                                                     *geo, threads=th))
+                done, total, what = n, c["N"], "images"
+            else:
+                P, Q = conv_geometry(c)
+                size = {"dgrad": c["N"] * c["H"] * c["W"] * c["C"], "wgrad": c["K"] * c["R"] * c["S"] * c["C"]}[
+                    c["kind"]]
+                fn = oracle.conv2d_dgrad_nhwc_sample if c["kind"] == "dgrad" else oracle.conv2d_wgrad_nhwc_sample
+
+                def run(n):
+                    idx = np.random.default_rng(0).integers(0, size, n)
+                    fn(c["N"], c["H"], c["W"], c["C"], c["K"], c["R"], c["S"], a0, rest[0], dt, idx, c["sh"], c["sw"],
+                       c["ph"], c["pw"], c["dh"], c["dw"], threads=th)
+                n, t = sized(run, 4 * th, size)
+                done, total, what = n, size, "sampled outputs"
+            flops, _ = workload_cost(c)
+            full_s = t * total / done
+            row = {"workload": name, "threads": oracle.last_threads(), "sample": f"{done} of {total} {what}",
+                   "sample_s": float(f"{t:.4g}"), "full_s_extrapolated": float(f"{full_s:.4g}"),
+                   "gflops": round(flops / full_s / 1e9, 2)}
+            log(f"{name:40s} threads {row['threads']:3d}  {row['sample']:32s} {t:9.4g} s -> {full_s:9.4g} s full, "
+                f"{row['gflops']:8.2f} GFLOP/s")
+            rows_out.append(row)
+    print(json.dumps({"oracle_times": rows_out, "host_cpus": os.cpu_count(),
+                      "note": "fp64 oracle, as it is; time per output element extrapolated to the whole workload"}),
+          flush=True)
+
+
+# Barrier ring against the per-stage ready/free counter ring: each pair differs in the ring_sync field only.
+RING_PAIRS = [
+    ("gemm_bf16_8192x8192x8192", (256, 256, 32, 4, 8, 16, 0, 4), {}),
+    ("gemm_bf16_8192x8192x8192", (256, 256, 32, 3, 8, 32, 0, 4), {}),
+    ("gemm_bf16_8192x8192x8192", (256, 256, 32, 4, 8, 32, 0, 4), {}),
+    ("conv_bf16_n32_56x56_c256_k256_3x3", (256, 256, 32, 4, 8, 16, 0, 4), {}),
+    ("conv_bf16_n32_56x56_c256_k256_3x3", (256, 256, 32, 3, 8, 32, 0, 4), {}),
+    ("gemm_fp16_1000x1000x65536", (128, 128, 64, 4, 8, 16, 0, 4), {"stream_k": 256}),
+    ("gemm_bf16_2048x1024x16384", (128, 128, 64, 4, 8, 16, 0, 4), {"k_splits": 2}),
+]
+
+
+def run_ring_compare(reps, warmup, rounds=3):
+    """Times each pair of RING_PAIRS, alternating the two rings for `rounds` rounds of `reps` launches."""
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name, base, sched in RING_PAIRS:
+        flops, _ = workload_cost(inputs.WORKLOADS[name])
+        tunes = [igc.tune(base + (sync,), **sched) for sync in (0, 1)]
+        calls = [workload_call(name, stream, t)[0] for t in tunes]
+        ms = [[], []]
+        for _ in range(rounds):
+            for i in (0, 1):
+                ms[i].extend(time_launches(calls[i], stream, reps, warmup))
+        us = [float(np.mean(m)) * 1e3 for m in ms]
+        tile = ",".join(map(str, base)) + ",{0|1}" + "".join(f" {k}={v}" for k, v in sched.items())
+        row = {"workload": name, "tile": tile,
+               "barrier_us": round(us[0], 1), "counters_us": round(us[1], 1),
+               "barrier_tflops": round(flops / us[0] / 1e6, 1), "counters_tflops": round(flops / us[1] / 1e6, 1),
+               "counters_over_barrier": round(us[1] / us[0], 3)}
+        log(f"{name:36s} {row['tile']:40s} barrier {us[0]:8.1f} us  counters {us[1]:8.1f} us  "
+            f"ratio {row['counters_over_barrier']:.3f}")
+        rows.append(row)
+        del calls
+        torch.cuda.empty_cache()
+    print(json.dumps({"ring_compare": rows, "launches_per_ring": reps * rounds, "warmup": warmup,
+                      "note": "rings alternate in rounds; HIP events on the launch stream around each launch"}),
           flush=True)
 
 
@@ -192,6 +352,13 @@ def main():
     ap.add_argument("--suite", action="store_true",
                     help="instead of the step: time every named workload in implicit_gemm_conv_amd/inputs.py with the "
                          "built-in tile and print one JSON line with all of them")
+    ap.add_argument("--only", type=str, default=None, help="with --suite: comma-separated workload names")
+    ap.add_argument("--cold", action="store_true", help="with --suite: evict L2 and MALL before every launch")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="instead of the step: time the CPU oracle on every named workload (no GPU needed)")
+    ap.add_argument("--ring-compare", action="store_true",
+                    help="instead of the step: time the barrier ring against the per-stage counter ring on tile "
+                         "pairs that differ only in that, and print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run one plain device copy of MIB MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -200,13 +367,21 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.oracle_times:
+        run_oracle_times()
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     igc.lib()  # the HIP library must be built: no fallback
     if args.suite:
-        run_suite(max(args.steps, 5), max(args.warmup, 1))
+        run_suite(max(args.steps, 5), max(args.warmup, 1), args.only.split(",") if args.only else None, args.cold)
+        if args.copy_calibration:
+            copy_calibration(args.copy_calibration)
+        return
+    if args.ring_compare:
+        run_ring_compare(max(args.steps, 5), max(args.warmup, 1))
         return
     gtune = tuple(int(v) for v in args.tune.split(",")) if args.tune else None
     ctune = tuple(int(v) for v in args.conv_tune.split(",")) if args.conv_tune else None
@@ -284,14 +459,7 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us -> {value:.1f} TFLOP/s; host wall {wall / args.steps * 1e3:.3f} ms/step")
 
     if args.copy_calibration:
-        n = args.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {n * 4} bytes read and written once")
-        del src, dst
+        copy_calibration(args.copy_calibration)
 
     # MFMA-only ceiling with the same MFMA shape and wave count as the GEMM's tile (untimed)
     from implicit_gemm_conv_amd import probes

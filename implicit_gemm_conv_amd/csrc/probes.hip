@@ -141,6 +141,49 @@ __global__ __launch_bounds__(512) void dma_probe_kernel(const char* A, const cha
     }
 }
 
+// LDS read bandwidth: every wave streams reads of one kind over a 96 KB LDS
+// buffer (more than half the CU's LDS, so one workgroup per CU) with
+// consecutive lanes on consecutive addresses; KIND 0 = ds_read_b128 (the
+// GEMM's K-contiguous fragments), 1 = ds_read_b64_tr_b16 (its M/N-contiguous
+// fragments), 2 = ds_read_b64.
+constexpr int kLdsProbeBytes = 96 * 1024;
+
+template <int KIND>
+__global__ __launch_bounds__(1024) void lds_probe_kernel(uint32_t* sink, uint32_t* clk, int iters) {
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsProbeBytes];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int i = threadIdx.x * 4; i < kLdsProbeBytes; i += blockDim.x * 4) *(uint32_t*)(lds + i) = i * 2654435761u;
+    __syncthreads();
+    constexpr int BPL = KIND == 0 ? 16 : 8;  // bytes per lane
+    constexpr int PER = 64 * BPL;            // bytes per wave instruction
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    uint32_t x = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // (it * 8 + j) * nw + wave instruction slots, wrapped inside the buffer
+            const uint32_t off = ((uint32_t)((it * 8 + j) * nw + wave) * PER) % kLdsProbeBytes + lane * BPL;
+            if constexpr (KIND == 0) {
+                const i16x8_t v = *(IGC_LDS i16x8_t*)((IGC_LDS char*)lds + off);
+                x ^= (uint32_t)v[0] ^ ((uint32_t)v[7] << 16);
+            } else if constexpr (KIND == 1) {
+                const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((IGC_LDS i16x4_t*)((IGC_LDS char*)lds + off));
+                x ^= (uint32_t)v[0] ^ ((uint32_t)v[3] << 16);
+            } else {
+                const i16x4_t v = *(IGC_LDS i16x4_t*)((IGC_LDS char*)lds + off);
+                x ^= (uint32_t)v[0] ^ ((uint32_t)v[3] << 16);
+            }
+        }
+    }
+    sink[blockIdx.x * blockDim.x + threadIdx.x] = x;
+    __syncthreads();
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = (uint32_t)(c1 - c0);
+        clk[2 * blockIdx.x + 1] = (uint32_t)(r1 - r0);
+    }
+}
+
 }  // namespace igc
 
 using namespace igc;
@@ -187,6 +230,23 @@ igc_status_t igc_probe_dma(int bk, int operands, const void* A, const void* B, i
     void* args[] = {&a, &b, &c};
     (void)hipGetLastError();
     if (hipLaunchKernel(fn, dim3(grid), dim3(512), args, 0, (hipStream_t)stream) != hipSuccess) return IGC_ERR_HIP;
+    return IGC_OK;
+}
+
+igc_status_t igc_probe_lds(int kind, int waves, int iters, int grid, void* sink, int64_t sink_bytes, void* clk,
+                           int64_t clk_bytes, igc_stream_t stream) {
+    if (kind < 0 || kind > 2 || waves < 1 || waves > 16 || iters < 1 || grid < 1 || !sink || !clk)
+        return IGC_ERR_INVALID_VALUE;
+    if (sink_bytes < (int64_t)grid * 64 * waves * 4 || clk_bytes < (int64_t)grid * 8) return IGC_ERR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(sink) & 3) || (reinterpret_cast<uintptr_t>(clk) & 3)) return IGC_ERR_MISALIGNED;
+    const void* fn = kind == 0 ? (const void*)&lds_probe_kernel<0>
+                               : (kind == 1 ? (const void*)&lds_probe_kernel<1> : (const void*)&lds_probe_kernel<2>);
+    uint32_t* s = (uint32_t*)sink;
+    uint32_t* c = (uint32_t*)clk;
+    void* args[] = {&s, &c, &iters};
+    (void)hipGetLastError();
+    if (hipLaunchKernel(fn, dim3(grid), dim3(64 * waves), args, 0, (hipStream_t)stream) != hipSuccess)
+        return IGC_ERR_HIP;
     return IGC_OK;
 }
 

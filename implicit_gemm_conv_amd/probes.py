@@ -33,6 +33,8 @@ def plib():
         L.igc_probe_mfma.restype = i32
         L.igc_probe_dma.argtypes = [i32, i32, p, p, i64, p, i64, p]
         L.igc_probe_dma.restype = i32
+        L.igc_probe_lds.argtypes = [i32, i32, i32, i32, p, i64, p, i64, p]
+        L.igc_probe_lds.restype = i32
         _plib = L
     return _plib
 
@@ -49,6 +51,11 @@ def igc_probe_dma(bk, operands, A, B, bytes_each, clk, clk_bytes, stream=None):
 SPEC_CLOCK_GHZ = 2.4
 PEAK_BF16_TFLOPS = 2516.6
 CUS = 256
+
+
+def igc_probe_lds(kind, waves, iters, grid, sink, sink_bytes, clk, clk_bytes, stream=None):
+    return plib().igc_probe_lds(kind, waves, iters, grid, igc._ptr(sink), sink_bytes, igc._ptr(clk), clk_bytes,
+                                igc._stream(stream))
 
 
 def _clock(clk, n):
@@ -109,12 +116,37 @@ def dma_throughput(bk, operands, reps=3):
             "B/clk/CU": round(nbytes / CUS / (ms * 1e-3) / (ghz * 1e9), 1)}
 
 
+LDS_KINDS = {0: "ds_read_b128", 1: "ds_read_b64_tr_b16", 2: "ds_read_b64"}
+
+
+def lds_bandwidth(kind, waves=8, iters=4000, grid=256, reps=3):
+    """LDS read bytes per clock per CU: each workgroup's bytes over its own shader-clock cycles (one workgroup
+    per CU), median over workgroups, best of `reps` launches."""
+    import torch
+    sink = torch.empty(grid * 64 * waves, dtype=torch.int32, device="cuda")
+    clk = torch.zeros(2 * grid, dtype=torch.int32, device="cuda")
+    per_wg = waves * iters * 8 * 64 * (16 if kind == 0 else 8)
+    best = None
+    for _ in range(reps):
+        igc.check(igc_probe_lds(kind, waves, iters, grid, sink, sink.numel() * 4, clk, clk.numel() * 4))
+        torch.cuda.synchronize()
+        cyc = clk[0::2].cpu().numpy().astype(np.uint32).astype(np.float64)
+        bpc = float(np.median(per_wg / cyc))
+        if best is None or bpc > best[0]:
+            best = (bpc, _clock(clk, grid))
+    return {"read": LDS_KINDS[kind], "waves": waves, "B/clk/CU": round(best[0], 1), "ghz": round(best[1], 3)}
+
+
 def main():
     import torch
     torch.cuda.set_device(0)
     print("MFMA-only ceiling (wave tile of the GEMM kernels, random bf16 operands in registers):")
     for mfma, waves in ((16, 8), (32, 8), (16, 4), (32, 4)):
         print("  ", mfma_ceiling(mfma, waves))
+    print("LDS read bandwidth (one workgroup per CU, consecutive lanes on consecutive addresses):")
+    for kind in (0, 1, 2):
+        for waves in (4, 8, 16):
+            print("  ", lds_bandwidth(kind, waves))
     print("global->LDS tile loads of the 8192^3 GEMM alone (A row segment = 2*bk bytes; B rows 512 bytes):")
     for bk in (16, 32, 64):
         for ops in (1, 2, 3):

@@ -3,7 +3,7 @@
  * (libigc_probes.so).  They are not part of the GEMM / convolution ABI: they
  * bound it.  The "B200 TMA Pipeline Designer" page (section "Limitations")
  * says the best pipeline depth must be measured on real shapes and clocks;
- * these give the two ceilings the measurements are read against.
+ * these give the ceilings the measurements are read against.
  *
  * igc_probe_mfma: an MFMA-only stream with the wave tile of the GEMM kernels
  * (128 x 64 per wave with 8 waves, 128 x 128 with 4), `mfma` = 16
@@ -26,7 +26,15 @@
  * bytes_each >= 8192*8192*2 bytes (contents are not used); clk as above
  * (1024 workgroups).  Asynchronous on `stream`.
  *
- * Both return IGC_ERR_INVALID_VALUE for other parameter values or short
+ * igc_probe_lds: LDS read bandwidth.  `grid` workgroups of 64*waves threads
+ * (waves 1..16), each holding a 96 KB LDS buffer (so one workgroup per CU),
+ * run `iters` iterations of 8 reads per wave of one kind: kind 0 =
+ * ds_read_b128 (16 bytes per lane), 1 = ds_read_b64_tr_b16 (8 bytes), 2 =
+ * ds_read_b64 (8 bytes), consecutive lanes on consecutive addresses, i.e.
+ * grid*waves*iters*8*64*(16 or 8) bytes.  sink takes one uint32 per thread
+ * (grid*64*waves*4 bytes), clk as above.  Asynchronous on `stream`.
+ *
+ * All three return IGC_ERR_INVALID_VALUE for other parameter values or short
  * buffers, IGC_ERR_MISALIGNED for unaligned buffers (4 bytes; A and B 16),
  * IGC_ERR_HIP if the launch fails.
  */
@@ -42,6 +50,8 @@ extern "C" {
 igc_status_t igc_probe_mfma(int mfma, int waves, int iters, int grid, void *sink, int64_t sink_bytes, void *clk,
                             int64_t clk_bytes, igc_stream_t stream);
 igc_status_t igc_probe_dma(int bk, int operands, const void *A, const void *B, int64_t bytes_each, void *clk,
+                           int64_t clk_bytes, igc_stream_t stream);
+igc_status_t igc_probe_lds(int kind, int waves, int iters, int grid, void *sink, int64_t sink_bytes, void *clk,
                            int64_t clk_bytes, igc_stream_t stream);
 
 #ifdef __cplusplus

@@ -46,7 +46,7 @@ def test_probe_library_exports_every_declared_symbol():
     from implicit_gemm_conv_amd import probes
     L = ctypes.CDLL(probes.PROBES_PATH)
     names = declared_functions(PROBES_HEADER)
-    assert names == ["igc_probe_dma", "igc_probe_mfma"]
+    assert names == ["igc_probe_dma", "igc_probe_lds", "igc_probe_mfma"]
     assert all(hasattr(L, n) for n in names)
 
 
@@ -182,6 +182,25 @@ def test_probe_dma_validation(args, expect):
     a.update(args)
     st = probes.igc_probe_dma(a["bk"], a["operands"], a["A"], a["B"], a["bytes_each"], a["clk"], a["clk_bytes"],
                               stream=0)
+    assert st == expect, igc.igc_status_string(st)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(kind=3), igc.IGC_ERR_INVALID_VALUE),
+    (dict(kind=-1), igc.IGC_ERR_INVALID_VALUE),
+    (dict(waves=17), igc.IGC_ERR_INVALID_VALUE),
+    (dict(waves=0), igc.IGC_ERR_INVALID_VALUE),
+    (dict(iters=0), igc.IGC_ERR_INVALID_VALUE),
+    (dict(sink_bytes=256 * 8 * 64 * 4 - 4), igc.IGC_ERR_INVALID_VALUE),  # one word short
+    (dict(clk_bytes=256 * 8 - 4), igc.IGC_ERR_INVALID_VALUE),
+    (dict(clk=FAKE + 1), igc.IGC_ERR_MISALIGNED),
+])
+def test_probe_lds_validation(args, expect):
+    from implicit_gemm_conv_amd import probes
+    a = dict(kind=0, waves=8, iters=10, grid=256, sink=FAKE, sink_bytes=256 * 8 * 64 * 4, clk=FAKE, clk_bytes=256 * 8)
+    a.update(args)
+    st = probes.igc_probe_lds(a["kind"], a["waves"], a["iters"], a["grid"], a["sink"], a["sink_bytes"], a["clk"],
+                              a["clk_bytes"], stream=0)
     assert st == expect, igc.igc_status_string(st)
 
 

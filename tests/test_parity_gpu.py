@@ -2,9 +2,10 @@
 
 Bar: every output element within |y - ref| <= 1e-4*S + 1e-6 (+ half an ulp of
 a 16-bit output format), S = sum |a*b|; bit-exact where the inputs make every
-partial sum exact.  Covers the five named workloads (the small one in full,
-the large ones on sampled outputs at full size in the benchmark's launch
-configuration), boundary tiles, K not a multiple of the K tile, varied K-tile
+partial sum exact.  Covers the five named workloads at full size in the benchmark's launch
+configuration (the small ones and the small-grid deep-K ones in full; 8192^3
+and the 3x3 convolution on every edge tile, one interior tile per XCD residue
+and 1M samples), boundary tiles, K not a multiple of the K tile, varied K-tile
 counts for every compiled pipeline depth, all operand layouts, both input
 types, all output types, NaN padding that must never be read, and the
 convolution's padding/stride/dilation cases.
@@ -85,43 +86,81 @@ def test_workload_small_gemm_full():
     say(f"  max err/bound {r:.3g}")
 
 
-def sample_points(M, N, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = list(rng.integers(0, M, n))
-    cols = list(rng.integers(0, N, n))
-    # every element of the first and last 32 x 32 corner, and the last row / column
-    for r0, c0 in ((0, 0), (max(M - 32, 0), max(N - 32, 0)), (0, max(N - 32, 0)), (max(M - 32, 0), 0)):
-        for r in range(r0, min(r0 + 32, M)):
-            for c in range(c0, min(c0 + 32, N)):
-                rows.append(r)
-                cols.append(c)
-    for c in range(0, N, max(1, N // 512)):
-        rows.append(M - 1)
-        cols.append(c)
-    for r in range(0, M, max(1, M // 512)):
-        rows.append(r)
-        cols.append(N - 1)
-    return np.array(rows, np.int64), np.array(cols, np.int64)
+def max_err_over_s(y, ref, S):
+    return float(np.max(np.abs(np.asarray(y, np.float64) - ref) / np.maximum(S, 1e-300)))
 
 
-@pytest.mark.parametrize("name,out", [
-    ("gemm_bf16_8192x8192x8192", None),
-    ("gemm_bf16_8192x8192x8192", "f32"),   # the accumulator itself at the strict bound
-    ("gemm_bf16_2048x1024x16384", None),
-    ("gemm_fp16_1000x1000x65536", None),
-])
-def test_workload_large_gemm_sampled(name, out):
+@pytest.mark.parametrize("name", ["gemm_bf16_2048x1024x16384", "gemm_fp16_1000x1000x65536"])
+def test_workload_small_grid_full(name):
+    """The small-grid, deep-K workloads in full with the built-in schedule (split-K or stream-K, fp32 output, the
+    accumulator at the strict bound): every output, so every split seam and every owner-collected tile."""
     cfg = inputs.WORKLOADS[name]
-    out = out or cfg["out"]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    say(f"workload {name} -> {out}")
+    t = igc.igc_default_tune(M, N, K)
+    say(f"workload {name} -> {cfg['out']} tile {t.astuple()} k_splits={t.k_splits} stream_k={t.stream_k}")
     A, lda, B, ldb = inputs.workload_operands(name)
-    y, _ = run_gemm(M, N, K, A, lda, cfg["la"], B, ldb, cfg["lb"], out=out, dtype=cfg["dtype"])
-    rows, cols = sample_points(M, N, 12000, seed=cfg["seed"])
-    ref, S = oracle.gemm_sample(M, N, K, A, lda, LAYOUT[cfg["la"]], B, ldb, LAYOUT[cfg["lb"]],
-                                oracle.FP16 if cfg["dtype"] == "fp16" else oracle.BF16, rows, cols)
-    r = assert_close(y[rows, cols], ref, S, out, name)
-    say(f"  {rows.size} sampled outputs, max err/bound {r:.3g}")
+    y, _ = run_gemm(M, N, K, A, lda, cfg["la"], B, ldb, cfg["lb"], out=cfg["out"], dtype=cfg["dtype"])
+    ref, S = oracle_gemm(M, N, K, A, lda, cfg["la"], B, ldb, cfg["lb"], cfg["dtype"])
+    r = assert_close(y, ref, S, cfg["out"], name)
+    say(f"  {y.size} outputs, max err/bound {r:.3g}, max err/S {max_err_over_s(y, ref, S):.3g}")
+
+
+def tile_plan(TM, TN, seed):
+    """Tiles to check whole: every tile on the grid's edge, and one interior tile for each residue of the tile id
+    (row-major over the tile grid) modulo the 8 XCDs."""
+    edge = [(i, j) for i in range(TM) for j in range(TN) if i in (0, TM - 1) or j in (0, TN - 1)]
+    rng = np.random.default_rng(seed)
+    inner = []
+    inner_cols = range(1, TN - 1) if TN > 2 else range(TN)  # a grid one or two tiles wide has no inner column
+    for r in range(8):
+        ids = [i * TN + j for i in range(1, TM - 1) for j in inner_cols if (i * TN + j) % 8 == r]
+        if ids:
+            t = int(rng.choice(ids))
+            inner.append((t // TN, t % TN))
+    return edge, inner
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_workload_large_gemm_dense(out):
+    """8192^3 with the built-in tile: every element of every edge tile (the first and last tile rows and columns)
+    and of one interior tile per XCD residue, plus 1M seeded samples; bf16 output and fp32 (the accumulator at the
+    strict bound)."""
+    name = "gemm_bf16_8192x8192x8192"
+    cfg = inputs.WORKLOADS[name]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    t = igc.igc_default_tune(M, N, K)
+    BM, BN = t.bm, t.bn
+    say(f"workload {name} -> {out} tile {t.astuple()}")
+    A, lda, B, ldb = inputs.workload_operands(name)
+    assert cfg["la"] == "row" and cfg["lb"] == "row"
+    y, _ = run_gemm(M, N, K, A, lda, "row", B, ldb, "row", out=out)
+    A2, B2 = A.reshape(M, lda), B.reshape(K, ldb)
+    worst = 0.0
+    # edge bands: whole tile rows 0 and TM-1, whole tile columns 0 and TN-1
+    for r0 in (0, M - BM):
+        ref, S = oracle.gemm(BM, N, K, np.ascontiguousarray(A2[r0:r0 + BM]), lda, oracle.ROW_MAJOR, B, ldb,
+                             oracle.ROW_MAJOR, oracle.BF16)
+        assert_close(y[r0:r0 + BM], ref, S, out, f"{name} tile row at {r0}")
+        worst = max(worst, max_err_over_s(y[r0:r0 + BM], ref, S))
+    for c0 in (0, N - BN):
+        Bc = np.ascontiguousarray(B2[:, c0:c0 + BN])
+        ref, S = oracle.gemm(M, BN, K, A, lda, oracle.ROW_MAJOR, Bc, BN, oracle.ROW_MAJOR, oracle.BF16)
+        assert_close(y[:, c0:c0 + BN], ref, S, out, f"{name} tile column at {c0}")
+        worst = max(worst, max_err_over_s(y[:, c0:c0 + BN], ref, S))
+    _, inner = tile_plan(M // BM, N // BN, cfg["seed"])
+    for tm, tn in inner:
+        r0, c0 = tm * BM, tn * BN
+        ref, S = oracle.gemm(BM, BN, K, np.ascontiguousarray(A2[r0:r0 + BM]), lda, oracle.ROW_MAJOR,
+                             np.ascontiguousarray(B2[:, c0:c0 + BN]), BN, oracle.ROW_MAJOR, oracle.BF16)
+        assert_close(y[r0:r0 + BM, c0:c0 + BN], ref, S, out, f"{name} interior tile ({tm},{tn})")
+        worst = max(worst, max_err_over_s(y[r0:r0 + BM, c0:c0 + BN], ref, S))
+    rng = np.random.default_rng(cfg["seed"] + 1)
+    rows, cols = rng.integers(0, M, 1 << 20), rng.integers(0, N, 1 << 20)
+    ref, S = oracle.gemm_sample(M, N, K, A, lda, oracle.ROW_MAJOR, B, ldb, oracle.ROW_MAJOR, oracle.BF16, rows, cols)
+    r = assert_close(y[rows, cols], ref, S, out, f"{name} samples")
+    worst = max(worst, max_err_over_s(y[rows, cols], ref, S))
+    n = 2 * BM * N + 2 * BN * M + len(inner) * BM * BN + rows.size
+    say(f"  ~{n} outputs checked ({len(inner)} interior tiles), max err/S {worst:.3g}, samples err/bound {r:.3g}")
 
 
 CONV_WORKLOADS = [n for n, c in inputs.WORKLOADS.items() if c["kind"] == "conv"]
@@ -130,25 +169,43 @@ CONV_WORKLOADS = [n for n, c in inputs.WORKLOADS.items() if c["kind"] == "conv"]
 @pytest.mark.parametrize("name,out", [(n, None) for n in CONV_WORKLOADS] +
                          [("conv_bf16_n32_56x56_c256_k256_3x3", "f32")])
 def test_workload_conv_sampled(name, out):
+    """Every named convolution at full size with the built-in tile: every output channel of the corner and edge
+    pixels of the first and last image (the padding taps), 200k seeded samples and, for the 3x3 workload, every
+    element of the first and last output tile and of one interior tile per XCD residue, plus 1M samples."""
     cfg = inputs.WORKLOADS[name]
     out = out or cfg["out"]
-    say(f"workload {name} -> {out}")
     x, w = inputs.workload_operands(name)
     geo = dict(sh=cfg["sh"], sw=cfg["sw"], ph=cfg["ph"], pw=cfg["pw"], dh=cfg["dh"], dw=cfg["dw"])
-    y, _ = run_conv(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], x, w, out=out, **geo)
+    Nn, C, K = cfg["N"], cfg["C"], cfg["K"]
+    P, Q = oracle.conv_out_hw(cfg["H"], cfg["W"], cfg["R"], cfg["S"], **geo)
+    M = Nn * P * Q
+    t = igc.igc_default_tune(M, K, cfg["R"] * cfg["S"] * C, op=igc.OP_CONV_FPROP)
+    say(f"workload {name} -> {out} tile {t.astuple()}")
+    y, _ = run_conv(Nn, cfg["H"], cfg["W"], C, K, cfg["R"], cfg["S"], x, w, out=out, **geo)
+    dense = name == "conv_bf16_n32_56x56_c256_k256_3x3"
     rng = np.random.default_rng(cfg["seed"])
-    idx = list(rng.integers(0, y.size, 12000))
-    P, Q, K = y.shape[1], y.shape[2], y.shape[3]
-    # every output channel of the four image corners of the first and last image (padding taps)
-    for n in (0, cfg["N"] - 1):
-        for p in (0, P - 1):
-            for q in (0, Q - 1):
-                idx += [((n * P + p) * Q + q) * K + k for k in range(K)]
-    idx = np.array(idx, np.int64)
-    ref, S = oracle.conv2d_nhwc_sample(cfg["N"], cfg["H"], cfg["W"], cfg["C"], cfg["K"], cfg["R"], cfg["S"], x, w,
-                                       oracle.BF16, idx, **geo)
-    r = assert_close(y.ravel()[idx], ref, S, out, name)
-    say(f"  {idx.size} sampled outputs, max err/bound {r:.3g}")
+    idx = [rng.integers(0, y.size, (1 << 20) if dense else 200000)]
+    for n in (0, Nn - 1):
+        for p in sorted({0, 1, P - 2, P - 1} & set(range(P))):
+            for q in sorted({0, 1, Q - 2, Q - 1} & set(range(Q))):
+                base = ((n * P + p) * Q + q) * K
+                idx.append(np.arange(base, base + K))
+    tiles = 0
+    if dense:
+        TM, TN = -(-M // t.bm), -(-K // t.bn)
+        edge, inner = tile_plan(TM, TN, cfg["seed"])
+        for tm, tn in [e for e in edge if e[0] in (0, TM - 1)] + inner:
+            pix = np.arange(tm * t.bm, min((tm + 1) * t.bm, M))
+            ch = np.arange(tn * t.bn, min((tn + 1) * t.bn, K))
+            idx.append((pix[:, None] * K + ch[None, :]).ravel())
+            tiles += 1
+    idx = np.concatenate(idx).astype(np.int64)
+    ref, S = oracle.conv2d_nhwc_sample(Nn, cfg["H"], cfg["W"], C, K, cfg["R"], cfg["S"], x, w, oracle.BF16, idx,
+                                       **geo)
+    got = y.ravel()[idx]
+    r = assert_close(got, ref, S, out, name)
+    say(f"  {idx.size} outputs checked ({tiles} whole tiles), max err/bound {r:.3g}, "
+        f"max err/S {max_err_over_s(got, ref, S):.3g}")
 
 
 # ---------------------------------------------------------------------------
