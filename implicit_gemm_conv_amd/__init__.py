@@ -32,7 +32,7 @@ EXPORTS = (
     "conv2d_nhwc_wgrad_implicit_gemm_fp16_ex",
     "igc_workspace_bytes", "igc_tune_supported", "igc_default_tune", "igc_tune_count", "igc_tune_get",
     "igc_tune_scope", "igc_tune_lds_bytes", "igc_status_string", "igc_take_device_error", "igc_debug_stream_k",
-    "igc_pool_allocations", "igc_ring_schedule", "igc_lds_chunk",
+    "igc_pool_allocations", "igc_ring_schedule", "igc_lds_chunk", "igc_stage_slot",
 )
 
 
@@ -120,6 +120,8 @@ def lib():
         L.igc_ring_schedule.restype = i32
         L.igc_lds_chunk.argtypes = [i32, i32, i32, i32]
         L.igc_lds_chunk.restype = i32
+        L.igc_stage_slot.argtypes = [i32, i32, i32]
+        L.igc_stage_slot.restype = i32
         _lib = L
     return _lib
 
@@ -311,6 +313,10 @@ def igc_ring_schedule(pipe_depth, k_tiles, half_stage=0):
 
 def igc_lds_chunk(k_contiguous, chunks_per_row, row, logical_chunk):
     return lib().igc_lds_chunk(k_contiguous, chunks_per_row, row, logical_chunk)
+
+
+def igc_stage_slot(row, slot, slots_per_row):
+    return lib().igc_stage_slot(row, slot, slots_per_row)
 
 
 def check(status):

@@ -645,6 +645,11 @@ int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chu
     return logical_chunk ^ swz_mn(row);
 }
 
+int igc_stage_slot(int row, int slot, int slots_per_row) {
+    if (row < 0 || slot < 0 || (slots_per_row != 16 && slots_per_row != 32) || slot >= slots_per_row) return -1;
+    return stage_slot(row, slot, slots_per_row);
+}
+
 int igc_ring_schedule(int D, int half, int KT, int* ev, int cap) {
     if (D < 1 || D > 8 || half < 0 || half > 1 || (half && D < 2) || KT < 0 || cap < 0 || (cap > 0 && !ev))
         return -1;

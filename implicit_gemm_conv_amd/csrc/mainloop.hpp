@@ -1013,16 +1013,20 @@ __device__ __forceinline__ IGC_LDS char* stage_piece(int w) {
     }
 }
 
-// Chunk swizzle of a staged row of CPR 16-byte chunks.  Rows of 256 bytes or
-// more start on the same bank, so the row itself spreads them; 128-byte rows
-// alternate between the two bank halves with the row's parity, so row/2
-// spreads each half.  Either way the 16 (or 32) rows an MFMA block writes at
-// one column land on distinct banks, and every read of whole rows is
-// conflict-free.
-template <int CPR>
-__device__ __forceinline__ int stage_swz(int row) {
-    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "staged rows of 128 bytes or more");
-    return CPR >= 16 ? (row & (CPR - 1)) : ((row >> 1) & (CPR - 1));
+// Staged-row swizzle, in 8-byte slots: slot s of row r of a staged row of
+// `slots` slots (16: 128 bytes, 32: 256 bytes) is stored at s ^ f(r).  A
+// 64-bit staging write puts 16 (or 32) consecutive rows at one column of an
+// MFMA block, every row starting on the same bank, so f must spread them:
+// f(r) differs for any 16 consecutive rows modulo 16 slots (16 lanes per
+// clock on 32 banks of 4 bytes, the model under which the earlier map's
+// measured conflicts appear) and, for any 32 lanes, lands them on distinct
+// 8-byte units of a 256-byte cycle (32 lanes per clock on 64 banks).  The map
+// XORs one value into both halves of a 16-byte chunk, so a 16-byte read finds
+// a logical chunk whole in one physical chunk, halves swapped when f is odd.
+IGC_HD inline int stage_slot(int row, int slot, int slots) {
+    const int f = slots >= 32 ? (((row & 15) << 1) | ((row >> 3) & 1)) ^ ((row >> 4) & 1)
+                              : (row & 15) ^ ((row >> 4) & 1);
+    return slot ^ f;
 }
 
 // Blocks I0 .. I0+NI-1 (MFMA block rows) of a wave's sub-tile, as ESZ-byte
@@ -1034,6 +1038,7 @@ __device__ __forceinline__ void stage_rows(ML& ml, const typename C::Acc (&acc)[
     constexpr int MI = C::MI, NH = C::NH, NG = MI == 32 ? 4 : 1;
     constexpr int RB = C::WTN * ESZ;  // bytes per staged row
     constexpr int CPR = RB / 16;      // 16-byte chunks per staged row
+    static_assert(ESZ == 2 && (CPR == 8 || CPR == 16), "16-bit rows of 128 or 256 bytes");
     const int lane = ml.lane;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -1043,12 +1048,10 @@ __device__ __forceinline__ void stage_rows(ML& ml, const typename C::Acc (&acc)[
             for (int g = 0; g < NG; ++g) {
                 const int row = MI * i + lane % MI;
                 const int byte = (MI * j + 4 * NH * g + 4 * (lane / MI)) * ESZ;
-                IGC_LDS char* a = reg + row * RB + (((byte >> 4) ^ stage_swz<CPR>(row)) << 4) + (byte & 15);
+                IGC_LDS char* a = reg + row * RB + (stage_slot(row, byte >> 3, 2 * CPR) << 3);
                 const float v0 = acc[I0 + i][j][4 * g + 0], v1 = acc[I0 + i][j][4 * g + 1];
                 const float v2 = acc[I0 + i][j][4 * g + 2], v3 = acc[I0 + i][j][4 * g + 3];
-                if constexpr (ESZ == 4) {
-                    *(IGC_LDS f32x4_t*)a = f32x4_t{v0, v1, v2, v3};
-                } else if (kind == OUT_BF16) {
+                if (kind == OUT_BF16) {
                     typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
                     *(IGC_LDS bf16x4_t*)a = bf16x4_t{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
                 } else {
@@ -1065,7 +1068,11 @@ __device__ __forceinline__ void stage_rows(ML& ml, const typename C::Acc (&acc)[
 #pragma unroll
     for (int q = 0; q < NI * MI / RPI; ++q) {
         const int row = q * RPI + lane / CPR, c = lane % CPR;
-        const u32x4_t v = *(const IGC_LDS u32x4_t*)(reg + row * RB + ((c ^ stage_swz<CPR>(row)) << 4));
+        // slots 2c and 2c+1 stay one 16-byte chunk (the map XORs one value into both), in swapped order
+        // when slot 2c lands odd
+        const int p0 = stage_slot(row, 2 * c, 2 * CPR);
+        u32x4_t v = *(const IGC_LDS u32x4_t*)(reg + row * RB + ((p0 >> 1) << 4));
+        if (p0 & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
         *(u32x4_t*)((char*)dst + ((gm0 + row) * ldc + gn0) * ESZ + c * 16) = v;
     }
     // reads done before the piece is written again

@@ -360,6 +360,16 @@ int igc_ring_schedule(int pipe_depth, int half_stage, int k_tiles, int *events, 
  */
 int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chunk);
 
+/*
+ * LDS swizzle of the output epilogue's staged rows, for inspection and
+ * testing on the host.  A wave stages its 16-bit output sub-tile in LDS as
+ * rows of slots_per_row 8-byte slots (16: 128-byte rows, 32: 256-byte rows);
+ * logical slot `slot` of row `row` is stored at the returned physical slot of
+ * the same row.  Returns -1 for a negative row, a slot outside the row or
+ * another row width.  This is the map the kernels use.
+ */
+int igc_stage_slot(int row, int slot, int slots_per_row);
+
 #ifdef __cplusplus
 }
 #endif
