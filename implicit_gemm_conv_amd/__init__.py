@@ -262,7 +262,7 @@ def igc_tune_get(i):
     return t if lib().igc_tune_get(i, ctypes.byref(t)) else None
 
 
-SCOPE_ALL, SCOPE_STREAM_K = 1, 2
+SCOPE_ALL, SCOPE_STREAM_K, SCOPE_CONV_FPROP = 1, 2, 4
 
 
 def igc_tune_scope(i):
@@ -275,7 +275,8 @@ def igc_tune_lds_bytes(t):
 
 def tunes(scope=0):
     """Compiled (bm, bn, bk, pipe_depth, waves, mfma, half_stage, loader_waves, ring_sync) configurations whose
-    scope includes every bit of `scope` (SCOPE_ALL: every type, layout and operation; SCOPE_STREAM_K)."""
+    scope includes every bit of `scope` (SCOPE_ALL: every type, layout and operation; SCOPE_STREAM_K;
+    SCOPE_CONV_FPROP: the complete forward convolution)."""
     return [igc_tune_get(i).astuple() for i in range(igc_tune_count()) if igc_tune_scope(i) & scope == scope]
 
 

@@ -6,8 +6,9 @@
 Each tile configuration listed in csrc/tile_configs.hpp is compiled from
 csrc/instances.hip as one object per operation family (bf16 GEMM, fp16 GEMM,
 forward convolution, data gradient, filter gradient; study-only
-configurations build the bf16 GEMM and forward convolution only), all in
-parallel, then linked with the host-side C ABI (csrc/igc_lib.hip,
+configurations build the bf16 and fp16 GEMM and the bf16 forward convolution,
+forward-convolution configurations the study GEMMs and the complete forward
+convolution), all in parallel, then linked with the host-side C ABI (csrc/igc_lib.hip,
 csrc/registry.hip) and the split-K reduction (csrc/split_reduce.hip).
 """
 import concurrent.futures
@@ -63,12 +64,15 @@ def instance_units(configs=None):
     for (bm, bn, bk, d, w, mi, h, lw, sy, scope) in (configs or tile_configs()):
         if only and f"{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}x{lw}x{sy}" not in only:
             continue
-        full, sk = scope & 1, (scope >> 1) & 1
-        for fam in (FAMILIES_FULL if full else FAMILIES_STUDY):
+        full, sk, conv = scope & 1, (scope >> 1) & 1, (scope >> 2) & 1
+        fams = [(f, full) for f in (FAMILIES_FULL if full else FAMILIES_STUDY)]
+        if conv and not full:  # the study GEMMs, and the forward convolution complete
+            fams = [(0, 0), (1, 0), (2, 1)]
+        for fam, fam_full in fams:
             obj = os.path.join(OBJ_DIR, f"inst_{bm}x{bn}x{bk}x{d}x{w}x{mi}x{h}x{lw}x{sy}_f{fam}.o")
             units.append([HIPCC, *FLAGS, f"-DIGC_BM={bm}", f"-DIGC_BN={bn}", f"-DIGC_BK={bk}", f"-DIGC_D={d}",
                           f"-DIGC_W={w}", f"-DIGC_MI={mi}", f"-DIGC_HALF={h}", f"-DIGC_LW={lw}", f"-DIGC_SYNC={sy}",
-                          f"-DIGC_FULL={full}", f"-DIGC_SK={sk}", f"-DIGC_FAMILY={fam}", "-c",
+                          f"-DIGC_FULL={fam_full}", f"-DIGC_SK={sk}", f"-DIGC_FAMILY={fam}", "-c",
                           os.path.join(CSRC, "instances.hip"),
                           "-o", obj])
     return units

@@ -332,7 +332,6 @@ struct Cfg {
     static_assert(!SPREAD || Ring::wait_units(U) * (TA::IPW > TB::IPW ? TA::IPW : TB::IPW) < 64,
                   "vmcnt cannot express that many loads in flight");
     static_assert(SPREAD || HALF == 0, "odd rings are refilled during compute");
-    static_assert(LPT % KK == 0, "loads must split evenly over the k-steps");
 };
 
 // Per-lane DMA state of one operand: offsets of the chunks this lane fetches
@@ -1268,7 +1267,8 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
                     ml.template issue_units_part<kk, KK, op1, op2>(t1, d1, t2, d2);
                     ml.read_frags(slot_a<C, u>(), slot_b<C, u>(), kk + 1, fa[pn], fb[pn]);
                     ML::mma(acc, fa[pc], fb[pc]);
-                    interleave<NMF, DSR, C::LPT / KK>();
+                    // the loads of part kk of issue_units_part (both units: LPT in all)
+                    interleave<NMF, DSR, (kk + 1) * C::LPT / KK - kk * C::LPT / KK>();
                     __builtin_amdgcn_sched_barrier(0);
                 });
                 constexpr int pl = (p0 + KK - 1) & 1;  // set of the last k-step; the next tile's first uses pl^1

@@ -68,7 +68,19 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op) {
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     const int64_t r256 = (t256 + kCUs - 1) / kCUs, r128 = (t128 + kCUs - 1) / kCUs;
-    if (t256 > 0 && r256 * 100 <= r128 * 31) return big;
+    if (t256 > 0 && r256 * 100 <= r128 * 31) {
+        // A forward convolution whose 256-row tiles leave a last round partly idle may fill its rounds
+        // better with 224-row tiles (7/8 of the work each): the 3x3 workload's 100,352 output pixels
+        // make 392 tiles of 256 (1.53 rounds over 256 CUs) but 448 of 224 (1.75 rounds of 7/8 the
+        // work).  Taken when whole rounds times rows per tile is smaller, and only where it is built.
+        if (op == IGC_OP_CONV_FPROP) {
+            const igc_tune_t b224 = {224, 256, 64, 2, 8, 16, 1, 4, 1, 0, 0, 0};
+            const int64_t t224 = ((M + 223) / 224) * ((N + 255) / 256), r224 = (t224 + kCUs - 1) / kCUs;
+            const Instance* e = find_instance(b224, false, true, true, IGC_OP_CONV_FPROP);
+            if (e && e->full && r224 * 224 < r256 * 256) return b224;
+        }
+        return big;
+    }
     // Small tiles.  When even they leave CUs idle and K is deep (at least 2048
     // per CU's share), the K work is spread over every CU: a 2-way split when
     // the tiles fill exactly half the CUs (each workgroup one half of a tile,

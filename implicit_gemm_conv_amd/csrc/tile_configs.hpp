@@ -9,12 +9,15 @@
 // variant -- without it only the bf16 and fp16 GEMM with row-major A (both B
 // layouts, K a multiple of 8) and the bf16 forward convolution (whole filter
 // taps per K tile), which is what the stage-budget, synchronisation and
-// small-grid studies time; bit 1 also builds the stream-K kernel.  The build
-// script reads this list and compiles one object per configuration and
-// operation family.
+// small-grid studies time; bit 1 also builds the stream-K kernel; bit 2
+// builds those study GEMMs plus the bf16 and fp16 forward convolution with
+// every loop variant (for tiles whose rows cannot serve M/N-contiguous
+// operands, such as 224-row tiles).  The build script reads this list and
+// compiles one object per configuration and operation family.
 #pragma once
 #define IGC_FOR_EACH_TILE(X)                  \
     X(256, 256, 64, 2, 8, 16, 1, 4, 0, 3)     \
+    X(224, 256, 64, 2, 8, 16, 1, 4, 0, 4)     \
     X(128, 128, 64, 4, 8, 16, 0, 4, 0, 3)     \
     X(256, 256, 32, 4, 8, 16, 0, 4, 0, 3)     \
     X(128, 128, 64, 4, 4, 32, 0, 0, 0, 2)     \

@@ -283,9 +283,10 @@ int igc_default_tune(igc_op_t op, int64_t M, int64_t N, int64_t K, igc_tune_t *o
  * igc_tune_scope(i) is a bit mask of what configuration i is built for: IGC_SCOPE_ALL (every input type,
  * operand layout, operation and loop variant; without it only the bf16 and fp16 GEMM with row-major A and
  * K % 8 == 0, and the bf16 forward convolution with whole filter taps per K tile and filters of at most
- * 16 x 16 -- other calls are IGC_ERR_UNSUPPORTED) and IGC_SCOPE_STREAM_K (stream-K schedules; without it
- * a tune with stream_k > 0 is IGC_ERR_UNSUPPORTED); 0 for an index out of range. */
-enum { IGC_SCOPE_ALL = 1, IGC_SCOPE_STREAM_K = 2 };
+ * 16 x 16 -- other calls are IGC_ERR_UNSUPPORTED), IGC_SCOPE_STREAM_K (stream-K schedules; without it
+ * a tune with stream_k > 0 is IGC_ERR_UNSUPPORTED) and IGC_SCOPE_CONV_FPROP (the bf16 and fp16 forward
+ * convolution with every loop variant, besides the GEMMs with row-major A); 0 for an index out of range. */
+enum { IGC_SCOPE_ALL = 1, IGC_SCOPE_STREAM_K = 2, IGC_SCOPE_CONV_FPROP = 4 };
 int igc_tune_count(void);
 int igc_tune_get(int i, igc_tune_t *out);
 int igc_tune_scope(int i);

@@ -212,6 +212,7 @@ def test_tune_table_fits_lds():
     assert set(igc.tunes(igc.SCOPE_ALL | igc.SCOPE_STREAM_K)) >= {(256, 256, 64, 2, 8, 16, 1, 4, 0),
                                                                   (256, 256, 32, 4, 8, 16, 0, 4, 0),
                                                                   (128, 128, 64, 4, 8, 16, 0, 4, 0)}
+    assert C224 in igc.tunes(igc.SCOPE_CONV_FPROP)
     for (bm, bn, bk, d, w, mi, h, lw, sy) in tunes:
         assert 1 <= lw <= w and w % lw == 0
         lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw, sy))
@@ -233,15 +234,18 @@ def test_tune_table_fits_lds():
 T25 = (256, 256, 64, 2, 8, 16, 1, 4, 0)   # 256 x 256 x 64, two and a half stages: GEMM and forward convolution
 BIG = (256, 256, 32, 4, 8, 16, 0, 4, 0)   # 256 x 256 x 32, four stages: data gradient
 S8 = (128, 128, 64, 4, 8, 16, 0, 4, 0)    # 128 x 128 x 64, 8 waves: small grids
+C224 = (224, 256, 64, 2, 8, 16, 1, 4, 0)  # 224 x 256 x 64: forward convolutions whose 256-row tiles fill rounds badly
 
 
 @pytest.mark.parametrize("shape,op,expect", [
     ((8192, 8192, 8192), igc.OP_GEMM, (T25, 1, 0, 0)),               # 1024 tiles of 256x256: data-parallel
-    ((100352, 256, 2304), igc.OP_CONV_FPROP, (T25, 1, 0, 0)),        # the 3x3 conv's GEMM view: 392 tiles
+    ((100352, 256, 2304), igc.OP_CONV_FPROP, (C224, 1, 0, 0)),       # the 3x3 conv: 392 tiles of 256 rows (1.53
+                                                                     # rounds) but 448 of 224 (1.75 rounds of 7/8)
     ((100352, 256, 2304), igc.OP_CONV_DGRAD, (BIG, 1, 0, 0)),        # its data gradient: the 32-deep ring
     ((100352, 256, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
-    ((25088, 512, 2304), igc.OP_CONV_FPROP, (T25, 1, 0, 0)),         # stride-2 conv: 196 big tiles (1 round) beat
-                                                                     # 784 small ones (4 rounds)
+    ((25088, 512, 2304), igc.OP_CONV_FPROP, (C224, 1, 0, 0)),        # stride-2 conv: 196 big tiles (1 round) beat
+                                                                     # 784 small ones (4 rounds); 224 of 224 rows
+                                                                     # still make one round, of 7/8 the work
     ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
     ((256, 2304, 100352), igc.OP_CONV_WGRAD, (S8, 1, 256, 0)),       # the conv's filter gradient: 36 tiles, deep K
     ((2048, 1024, 16384), igc.OP_GEMM, (S8, 2, 0, 0)),               # 128 tiles of 128x128 = half the CUs: 2-way split

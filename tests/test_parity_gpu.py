@@ -33,6 +33,7 @@ def _compiled_tunes(scope=0):
 
 ALL_TUNES = _compiled_tunes()
 FULL_TUNES = set(_compiled_tunes(1))   # every type, layout and operation
+FPROP_TUNES = set(_compiled_tunes(4))  # the complete forward convolution
 SK_TUNES = _compiled_tunes(2)          # stream-K kernel built
 BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0)
 
@@ -40,7 +41,7 @@ BIG, SMALL = (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 4, 32, 0, 4, 0
 def supports(tune, la="row", K=64, op="gemm"):
     """A configuration built for every type, layout and operation supports any call; a study configuration only
     GEMMs with row-major A and K % 8 == 0, and forward convolutions (checked by the caller's shapes)."""
-    if tuple(tune[:9]) in FULL_TUNES:
+    if tuple(tune[:9]) in FULL_TUNES or (op == "fprop" and tuple(tune[:9]) in FPROP_TUNES):
         return True
     return op in ("gemm", "fprop") and la == "row" and K % 8 == 0
 
