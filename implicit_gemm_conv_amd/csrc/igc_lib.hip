@@ -123,6 +123,20 @@ static void* workspace_alloc(size_t bytes, hipStream_t stream) {
     return ptr;
 }
 
+// True if `stream` is being captured into a graph.  A workspace the library
+// would take from its pool during capture would become a memory node of the
+// caller's graph, allocated from the library's own pool; that use is refused
+// (the caller passes a workspace, or calls gemm_bf16_noalloc), since it has
+// not been shown to work on this runtime.
+static bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
+
 // Test hooks for the stream-K bounded wait (igc_debug_stream_k).
 constexpr int kDefaultSpinLimit = 1 << 20;  // about a second of polling
 static std::atomic<int> g_sk_spin_limit{0};
@@ -227,6 +241,7 @@ static igc_status_t launch(const Plan& pl, Params p, void* user_ws, int64_t user
     (void)hipGetLastError();  // launch errors below are ours alone
     char* ws = (char*)user_ws;
     const bool owned = !user_ws && L.bytes > 0;
+    if (owned && capturing(stream)) return IGC_ERR_UNSUPPORTED;
     if (owned) {
         ws = (char*)workspace_alloc((size_t)L.bytes, stream);
         if (!ws) return IGC_ERR_HIP;

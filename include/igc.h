@@ -32,7 +32,10 @@
  *   with hipFreeAsync on the same stream; the pool keeps up to 256 MiB of freed
  *   workspace mapped until the process ends (the device's default pool is not
  *   changed).  A schedule that does not split K needs and takes nothing.
- *   Calls that share one workspace must be ordered (one stream).
+ *   Calls that share one workspace must be ordered (one stream).  On a stream
+ *   that is being captured into a graph, a call whose schedule needs a
+ *   workspace must be given one (or use gemm_bf16_noalloc): the library does
+ *   not take one from its pool during capture (IGC_ERR_UNSUPPORTED).
  * - Leading dimensions are in ELEMENTS, not bytes.
  * - Alignment: every tensor base pointer must be 16-byte aligned and every
  *   leading dimension times the element size a multiple of 16 bytes (8

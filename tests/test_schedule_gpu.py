@@ -1,8 +1,8 @@
 """GPU tests of the schedules around the mainloop: the stream-K bounded wait failing loudly, caller-owned
-workspaces (no allocation, same bits as the library's pool), and a stream-K call captured in a HIP graph and
-replayed with changed inputs (flags are cleared by a kernel inside the graph, so stale flags of an earlier replay
-never count as raised).  Results are compared with the CPU oracle or, where the schedule is the thing under test,
-with the eager call bit for bit (the summation order is fixed)."""
+workspaces (no allocation, same bits as the library's pool), and stream-K calls captured in HIP graphs and
+replayed with changed inputs (flags are cleared by a kernel inside the graph, so stale
+flags of an earlier replay never count as raised).  Results are compared with the CPU oracle or, where the
+schedule is the thing under test, with the eager call bit for bit (the summation order is fixed)."""
 import numpy as np
 import pytest
 import torch
@@ -157,6 +157,100 @@ def test_stream_k_graph_replay():
         C.fill_(float("nan"))
         synchronize()
         say(f"graph replay {r}")
+        graph.replay()
+        synchronize()
+        assert torch.equal(C, eager), f"replay {r} differs from the eager call"
+    assert igc.igc_take_device_error() == 0
+
+
+@pytest.mark.skip(reason="the per-stream workspace cache was taken out: the GPU run that added it and the capture "
+                         "test below faulted (illegal address) in the no-allocation test that runs after them")
+def test_cached_workspace_per_stream():
+    """Without a caller workspace, the first split call on a stream takes a workspace and later calls on that
+    stream reuse it (no allocation); a larger need grows it once; another stream gets its own; after
+    igc_release_workspaces the next call takes a new one.  Every result equals the caller-workspace run bit for
+    bit."""
+    M, N, K = 1024, 512, 4096
+    t4, t8 = igc.Tune(*SMALL[:8], 4, 0, 0, 0), igc.Tune(*SMALL[:8], 8, 0, 0, 0)  # K split into 4 and 8
+    A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", dtype="bf16", seed=93)
+    dA, dB = to_dev(A), to_dev(B)
+    synchronize()
+    assert igc.igc_release_workspaces() == igc.IGC_OK
+
+    def call(tune, ws=None):
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        igc.check(igc.gemm_bf16_ex(M, N, K, dA, lda, igc.ROW_MAJOR, dB, ldb, igc.ROW_MAJOR, C, N, igc.OUT_F32,
+                                   tune, ws))
+        return C
+
+    refs = {}
+    for t in (t4, t8):
+        need = igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K, t)
+        refs[t.k_splits] = call(t, torch.empty(need, dtype=torch.uint8, device="cuda"))
+    synchronize()
+    base = igc.igc_pool_allocations()
+    steps = [(t4, 1), (t4, 1), (t4, 1), (t8, 2), (t4, 2)]  # (tune, allocations so far): t8 needs twice t4's
+    for i, (t, want) in enumerate(steps):
+        say(f"cached workspace step {i}: k_splits={t.k_splits}")
+        y = call(t)
+        synchronize()
+        assert igc.igc_pool_allocations() - base == want, f"step {i}"
+        assert torch.equal(y, refs[t.k_splits]), f"step {i}"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        other = call(t4)
+    torch.cuda.current_stream().wait_stream(side)
+    synchronize()
+    assert igc.igc_pool_allocations() - base == 3, "another stream shares the workspace"
+    assert torch.equal(other, refs[4])
+    assert igc.igc_release_workspaces() == igc.IGC_OK
+    again = call(t4)
+    synchronize()
+    assert igc.igc_pool_allocations() - base == 4
+    assert torch.equal(again, refs[4])
+
+
+@pytest.mark.skip(reason="faulted the GPU (illegal address, reported in the no-allocation test that runs after it) "
+                         "while the library took a pool workspace inside the capture; such calls are now refused "
+                         "with IGC_ERR_UNSUPPORTED, and this case stays off the GPU until the cause is shown")
+def test_graph_capture_without_workspace():
+    """A stream-K call with no caller workspace captured in a HIP graph: under capture the workspace comes from
+    the pool as graph nodes (not from the stream's cached one); every replay with new inputs equals the eager
+    call bit for bit."""
+    M, N, K = 1024, 1024, 8192
+    assert igc.igc_default_tune(M, N, K).stream_k > 0
+    dA = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    dB = torch.empty(K * N, dtype=torch.int16, device="cuda")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def call():
+        igc.check(igc.gemm_bf16(M, N, K, dA, K, igc.ROW_MAJOR, dB, N, igc.ROW_MAJOR, C, N, igc.OUT_F32))
+
+    def load(seed):
+        A, _, B, _ = inputs.gemm_operands(M, N, K, "row", "row", dtype="bf16", seed=seed)
+        dA.copy_(torch.from_numpy(A.view(np.int16).ravel()))
+        dB.copy_(torch.from_numpy(B.view(np.int16).ravel()))
+
+    load(210)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up outside the capture: creates the pool
+    torch.cuda.current_stream().wait_stream(side)
+    synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    synchronize()
+    for r, seed in enumerate((211, 212)):
+        load(seed)
+        call()
+        synchronize()
+        eager = C.clone()
+        C.fill_(float("nan"))
+        synchronize()
+        say(f"graph replay without workspace {r}")
         graph.replay()
         synchronize()
         assert torch.equal(C, eager), f"replay {r} differs from the eager call"
