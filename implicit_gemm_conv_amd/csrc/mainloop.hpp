@@ -945,15 +945,18 @@ __device__ __forceinline__ void ring_barrier() {
     compiler_fence();
 }
 
-// blockIdx -> (tile_m, tile_n).  Workgroup i is dispatched to XCD i % 8, and
-// each XCD has its own L2: give every XCD a contiguous range of tile ids, and
-// walk that range GROUP_M tiles down M at a time so the tiles resident on one
-// XCD share A rows and B columns in its L2.
-__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int kGroupM, int& tm, int& tn) {
+// Workgroup i is dispatched to XCD i % 8, and each XCD has its own L2:
+// xcd_order gives every XCD a contiguous range of the `count` work ids.
+__device__ __forceinline__ int xcd_order(int wg, int count) {
     constexpr int kXcds = 8;
-    const int G = tiles_m * tiles_n;
-    const int q = G / kXcds, r = G % kXcds, x = wg % kXcds, i = wg / kXcds;
-    const int id = (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    const int q = count / kXcds, r = count % kXcds, x = wg % kXcds, i = wg / kXcds;
+    return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Tile id -> (tile_m, tile_n), walking GROUP_M tiles down M at a time, so that
+// a contiguous range of ids (the tiles resident on one XCD) shares A rows and
+// B columns in that XCD's L2.
+__device__ __forceinline__ void group_coords(int id, int tiles_m, int tiles_n, int kGroupM, int& tm, int& tn) {
     const int group = kGroupM * tiles_n;
     const int g = id / group;
     const int first_m = g * kGroupM;
@@ -961,6 +964,11 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
     const int in = id - g * group;
     tm = first_m + in % gm;
     tn = in / gm;
+}
+
+// blockIdx -> (tile_m, tile_n) for a grid of one workgroup per tile.
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int kGroupM, int& tm, int& tn) {
+    group_coords(xcd_order(wg, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
 }
 
 // Scheduling template for one k-step region: NM MFMAs with ND LDS reads and
@@ -1493,17 +1501,20 @@ __device__ __forceinline__ void finish_item(ML& ml, typename C::Acc (&acc)[C::FM
 }
 
 // The data-parallel kernel of loop variant V: one workgroup per output tile
-// (tile blockIdx % T in the XCD-aware order of tile_coords) and K split
-// blockIdx / T.  It keeps no schedule state across its K loop: the loops of
+// and K split.  It keeps no schedule state across its K loop: the loops of
 // the largest tiles sit at the register limit, and any state kept alive around
 // them spills inside.
 template <class C, int V>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(const Params p) {
     static_assert(variant_applies<C, V>(), "loop variant of another operation");
+    // work id = split * T + tile, in XCD order over the whole grid: with a K
+    // split every XCD takes whole splits (or contiguous runs of one split's
+    // tiles), so the A and B slices of a split are fetched into one L2 only
     const int T = p.tiles_m * p.tiles_n;
-    const int split = (int)blockIdx.x / T;
+    const int id = xcd_order((int)blockIdx.x, T * p.k_splits);
+    const int split = id / T;
     int tm, tn;
-    tile_coords((int)blockIdx.x - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    group_coords(id - split * T, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int64_t kbase = (int64_t)split * p.k_per_split;
     const int64_t kend = kbase + p.k_per_split < p.K ? kbase + p.k_per_split : p.K;
     run_tile<C, V>(p, tm, tn, kbase, kend, [&](auto& ml, auto& acc) __attribute__((always_inline)) {

@@ -88,10 +88,20 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op) {
     // split 79 us vs stream-K 82-87 us on 2048 x 1024 x 16384; stream-K 176 us
     // vs a 4-way split 194 us on 1000 x 1000 x 65536).
     if (t128 > 0 && t128 < kCUs && K / 2048 >= 2) {
-        if (t128 * 2 == kCUs)
+        if (t128 * 2 == kCUs) {
             small.k_splits = 2;
-        else
+        } else {
+            // A GEMM whose 256 x 256 tiles divide the CUs evenly into K splits of at least 2048 runs those
+            // (the partials are summed by the reduction kernel; measured on 1000 x 1000 x 65536: 16 splits
+            // 168-177 us against 186-190 for 128 x 128 stream-K); otherwise stream-K over every CU.
+            const int64_t S = t256 > 0 ? kCUs / t256 : 0;
+            if (op == IGC_OP_GEMM && S >= 2 && S * t256 == kCUs && K / S >= 2048) {
+                igc_tune_t t = {256, 256, 64, 2, 8, 16, 1, 4, 1, 0, 0, 0};
+                t.k_splits = (int)S;
+                return t;
+            }
             small.stream_k = (int)kCUs;
+        }
     }
     return small;
 }

@@ -249,7 +249,9 @@ C224 = (224, 256, 64, 2, 8, 16, 1, 4, 0)  # 224 x 256 x 64: forward convolutions
     ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
     ((256, 2304, 100352), igc.OP_CONV_WGRAD, (S8, 1, 256, 0)),       # the conv's filter gradient: 36 tiles, deep K
     ((2048, 1024, 16384), igc.OP_GEMM, (S8, 2, 0, 0)),               # 128 tiles of 128x128 = half the CUs: 2-way split
-    ((1000, 1000, 65536), igc.OP_GEMM, (S8, 1, 256, 0)),             # 64 tiles: stream-K
+    ((1000, 1000, 65536), igc.OP_GEMM, (T25, 16, 0, 0)),             # 16 big tiles split 16 ways fill the CUs
+    ((1000, 1000, 65536), igc.OP_CONV_FPROP, (S8, 1, 256, 0)),       # (a forward conv view stays stream-K)
+    ((1000, 512, 8192), igc.OP_GEMM, (S8, 1, 256, 0)),               # 8 big tiles: 32 splits of 256 are too short
     ((1000, 1000, 3000), igc.OP_GEMM, (S8, 1, 0, 0)),                # too little K to share
     ((100352, 64, 256), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),           # 1x1 conv with 64 outputs: 128-wide tiles
     ((11664, 256, 2304), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),          # 27x27 images: 46 big tiles vs 184 small
@@ -269,7 +271,8 @@ def test_workspace_bytes():
     assert ws(igc.OP_GEMM, 8192, 8192, 8192) == 0
     assert ws(igc.OP_CONV_FPROP, 100352, 256, 2304) == 0
     assert ws(igc.OP_GEMM, 2048, 1024, 16384) == 2 * 2048 * 1024 * 4
-    assert ws(igc.OP_GEMM, 1000, 1000, 65536) == 256 * 128 * 128 * 4 + 1024
+    assert ws(igc.OP_GEMM, 1000, 1000, 65536) == 16 * 1000 * 1000 * 4     # built-in: 256 x 256 tiles split 16
+    assert ws(igc.OP_GEMM, 1000, 512, 8192) == 256 * 128 * 128 * 4 + 1024  # built-in: stream-K over 256
     assert ws(igc.OP_GEMM, 1000, 1000, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
     assert ws(igc.OP_GEMM, 1000, 998, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
     # stream-K with fewer K units than workgroups: G clamps to the units (2 tiles x 1 unit of 256)
