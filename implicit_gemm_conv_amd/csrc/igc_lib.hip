@@ -29,9 +29,9 @@
 static __device__ __align__(256) int g_err_word;
 
 // Workspace of gemm_bf16_noalloc, for callers that cannot allocate: room for
-// the largest workspace the built-in choice asks for (stream-K over 256
-// workgroups of 128 x 128 fp32 partials, 16 MiB + 1 KiB, or a 2-way split of at
-// most 128 tiles of 128 x 128, 16 MiB).  Each GPU the library runs on holds its
+// stream-K over 256 workgroups of 128 x 128 fp32 partials (16 MiB + 1 KiB) and
+// for a 2-way split of at most 128 tiles of 128 x 128 (16 MiB); a built-in
+// schedule that needs more runs as that stream-K instead.  Each GPU the library runs on holds its
 // own copy until the process ends; calls that overlap on one GPU share it and
 // race.
 constexpr int64_t kScratchBytes = (16ll << 20) + 4096;
@@ -569,13 +569,22 @@ igc_status_t conv2d_nhwc_wgrad_implicit_gemm_fp16_ex(int N, int H, int W, int C,
 igc_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, igc_layout_t la,
                                const void* B, int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type,
                                igc_stream_t stream) {
-    // the built-in schedule, with its workspace in this device's scratch array
+    // the built-in schedule, with its workspace in this device's scratch array;
+    // when that schedule needs more (a K split of 256 x 256 tiles), 128 x 128
+    // stream-K over 256 workgroups, whose workspace always fits
     if (M < 0 || N < 0 || K < 0) return IGC_ERR_INVALID_VALUE;
-    const Plan pl = pick(nullptr, false, la == IGC_ROW_MAJOR, lb == IGC_COL_MAJOR, OP_GEMM, M, N, K);
-    if (pl.inst && layout_of(pl, M, N, K).bytes > kScratchBytes) return IGC_ERR_UNSUPPORTED;
+    const bool a_kc = la == IGC_ROW_MAJOR, b_kc = lb == IGC_COL_MAJOR;
+    const Plan pl = pick(nullptr, false, a_kc, b_kc, OP_GEMM, M, N, K);
+    const igc_tune_t* tune = nullptr;
+    static const igc_tune_t kFits = {128, 128, 64, 4, 8, 16, 0, 4, 1, 256, 0, 0};
+    if (pl.inst && layout_of(pl, M, N, K).bytes > kScratchBytes) {
+        const Plan alt = pick(&kFits, false, a_kc, b_kc, OP_GEMM, M, N, K);
+        if (!alt.inst || layout_of(alt, M, N, K).bytes > kScratchBytes) return IGC_ERR_UNSUPPORTED;
+        tune = &kFits;
+    }
     void* ws = scratch_ptr();
     if (!ws) return IGC_ERR_HIP;
-    return gemm_any(false, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, nullptr, ws, kScratchBytes,
+    return gemm_any(false, M, N, K, A, lda, la, B, ldb, lb, C, ldc, c_type, tune, ws, kScratchBytes,
                     (hipStream_t)stream);
 }
 

@@ -259,11 +259,13 @@ igc_status_t conv2d_nhwc_wgrad_implicit_gemm_fp16_ex(int N, int H, int W, int C,
  * tight serving loops, harnesses that forbid hipMalloc): the built-in
  * schedule, with its workspace (K-split or stream-K partial tiles and flags)
  * in a library-owned device array of 16 MiB + 4 KiB that each GPU holds until
- * the process ends.  The call allocates nothing and gives the same bits as
- * gemm_bf16.  Calls that overlap on one GPU share the array and race: order
- * them (one stream).  A shape whose schedule needs more than the array holds is
- * IGC_ERR_UNSUPPORTED (the built-in choice never does); IGC_ERR_HIP if the
- * array cannot be located on the current device; otherwise as gemm_bf16. */
+ * the process ends.  The call allocates nothing.  When the built-in schedule's
+ * workspace fits the array it runs that schedule and gives the same bits as
+ * gemm_bf16; otherwise (a K split of 256 x 256 tiles, e.g. 1024 x 1024 x 32768)
+ * it runs 128 x 128 stream-K over 256 workgroups, whose workspace always fits,
+ * with a different summation order.  Calls that overlap on one GPU share the
+ * array and race: order them (one stream).  IGC_ERR_HIP if the array cannot
+ * be located on the current device; otherwise as gemm_bf16. */
 igc_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, igc_layout_t la,
                                const void *B, int64_t ldb, igc_layout_t lb, void *C, int64_t ldc, igc_out_t c_type,
                                igc_stream_t stream);

@@ -1,7 +1,8 @@
 """The no-allocation GEMM entry point (gemm_bf16_noalloc, workspace in a library-owned device array) against
 gemm_bf16 through the C ABI: two calls in a row, the second smaller, both with schedules that use the workspace
-(a 2-way K split, then stream-K), each equal to gemm_bf16 bit for bit (same kernels, same fixed summation order) and within the
-oracle's bound, and no workspace taken from the library's pool."""
+(a 2-way K split, then stream-K), each equal to gemm_bf16 bit for bit (same kernels, same fixed summation order)
+and within the oracle's bound, and no workspace taken from the library's pool; and a shape whose built-in
+schedule outgrows the array, run as 128 x 128 stream-K."""
 import numpy as np
 import pytest
 import torch
@@ -45,4 +46,30 @@ def test_noalloc_matches_gemm_bf16():
         import oracle
         ref, S = oracle.gemm_sample(M, N, K, A, lda, 0, B, ldb, 0, oracle.BF16, rows, cols)
         assert_close(host_values(mine)[rows, cols], ref, S, "f32", f"noalloc {M}x{N}x{K}")
+    assert igc.igc_take_device_error() == 0
+
+
+def test_noalloc_falls_back_to_stream_k():
+    """A shape whose built-in schedule (16-way split of 256 x 256 tiles, 64 MiB of partials) outgrows the
+    array: the no-allocation call runs 128 x 128 stream-K over 256 workgroups instead, equal bit for bit to
+    that schedule run with a caller workspace, within the oracle's bound, and allocates nothing."""
+    M, N, K = 1024, 1024, 32768
+    t = igc.igc_default_tune(M, N, K)
+    assert t.k_splits == 16 and igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K) > (16 << 20) + 4096
+    fits = igc.tune((128, 128, 64, 4, 8, 16, 0, 4, 0), stream_k=256)
+    A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", dtype="bf16", a_dist=("normal", 1.0),
+                                          b_dist=("normal", 1.0), seed=17)
+    dA, dB = to_dev(A), to_dev(B)
+    say(f"noalloc fallback {M}x{N}x{K}")
+    before = igc.igc_pool_allocations()
+    mine = _call(igc.gemm_bf16_noalloc, M, N, K, dA, dB)
+    assert igc.igc_pool_allocations() == before, "gemm_bf16_noalloc took a pool workspace"
+    ws = torch.empty(igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K, fits), dtype=torch.uint8, device="cuda")
+    ref_lib = _call(lambda *a: igc.gemm_bf16_ex(*a, fits, ws), M, N, K, dA, dB)
+    assert torch.equal(mine, ref_lib), "gemm_bf16_noalloc differs from 128 x 128 stream-K"
+    rows = np.random.default_rng(17).integers(0, M, 3000)
+    cols = np.random.default_rng(18).integers(0, N, 3000)
+    import oracle
+    ref, S = oracle.gemm_sample(M, N, K, A, lda, 0, B, ldb, 0, oracle.BF16, rows, cols)
+    assert_close(host_values(mine)[rows, cols], ref, S, "f32", f"noalloc fallback {M}x{N}x{K}")
     assert igc.igc_take_device_error() == 0
