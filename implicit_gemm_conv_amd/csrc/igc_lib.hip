@@ -694,20 +694,22 @@ int igc_ring_schedule(int D, int half, int KT, int* ev, int cap) {
         emit(READ, t, 0, Ring::slot_of(U, 2 * t));
         emit(READ, t, 1, Ring::slot_of(U, 2 * t + 1));
     };
-    // the K loop is padded to whole ring periods with zero-filled tiles
+    // two-stage rings pad the K loop to whole ring periods with zero-filled
+    // tiles; spread rings run exactly KT tiles (a last, partial period after
+    // the loop), and the units their last tiles issue past KT land as zeros
     const int P = Ring::period(U);
     const int KTp = (KT + P - 1) / P * P;
     if (Ring::spread(U)) {
         for (int s = 0; s < U - 2; ++s) issue_unit(s);
         emit(WAIT, 0, -1, Ring::wait_units(U));
-        if (KTp > 0)
+        if (KT > 0)
             read_tile(0);
         else
             emit(BARRIER, 0, -1, 0);  // K == 0: the kernel reads zeros it never uses
-        for (int t = 0; t < KTp; ++t) {
+        for (int t = 0; t < KT; ++t) {
             issue_unit(2 * t + U - 2);  // both spread over tile t's k-steps
             issue_unit(2 * t + U - 1);
-            if (t + 1 < KTp) {
+            if (t + 1 < KT) {
                 emit(WAIT, t + 1, -1, Ring::wait_units(U));
                 read_tile(t + 1);
             } else {

@@ -1213,8 +1213,9 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
     // set (u*KK + kk) % 2, while the next k-step's fragments load into the other.
     i16x8_t fa[2][FM], fb[2][FN];
 
-    // The accumulators are never updated under a branch: every K tile of the
-    // padded loop runs the same MFMA sequence, so no copies of them are needed.
+    // The accumulators are never updated under a branch inside a loop: every
+    // K tile of a loop runs the same MFMA sequence, so no copies of them are
+    // needed (the guarded tiles of a partial last period follow the loop).
     constexpr int NMF = FM * FN;
     constexpr int DSR = ML::DS_READS;
     if constexpr (C::SPREAD) {
@@ -1251,8 +1252,8 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
             ring_barrier();
         }
         ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
-        for (int t0 = 0; t0 < KTp; t0 += P) {
-            static_for<0, P>([&](auto UU) __attribute__((always_inline)) {
+        // Tile t0+u of a period (u a constant, so every slot is one).
+        auto tile = [&](auto UU, const int t0) __attribute__((always_inline)) {
                 constexpr int u = UU;
                 const int t = t0 + u;
                 // the two units refilled during tile t
@@ -1298,9 +1299,17 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
                 ML::mma(acc, fa[pl], fb[pl]);
                 interleave<NMF, DSR, 0>();
                 __builtin_amdgcn_sched_barrier(0);
+        };
+        // Whole periods in the loop; the tiles of a last, partial period run
+        // after it, each under its own test (those past KT are skipped, though
+        // the loads the last tiles issue for them still go out, as zeros).
+        int t0 = 0;
+        for (; t0 + P <= KT; t0 += P) static_for<0, P>([&](auto UU) __attribute__((always_inline)) { tile(UU, t0); });
+        if (t0 < KT)
+            static_for<0, P - 1>([&](auto UU) __attribute__((always_inline)) {
+                if (t0 + (int)UU < KT) tile(UU, t0);
             });
-        }
-        wait_vmcnt<0>();  // the padding tiles past the loop are still landing in free slots
+        wait_vmcnt<0>();  // the loads past KT are still landing in free slots
         if constexpr (CTR) {
             if (late && (threadIdx.x & 63) == 0)
                 __builtin_amdgcn_raw_buffer_store_b32(1, make_rsrc(p.err_word), 0, 0, 1 | 16);

@@ -29,7 +29,11 @@
 //                          finished reading tile t
 //              read fragments of tile t+1, first k-step
 //              compute the last k-step of t (operands already in registers)
-//   epilogue : wait for everything (the trailing units are padding).
+//   epilogue : wait for everything (the trailing units, past the last tile,
+//              are out of range and land as zeros).
+// The loop body is unrolled by the ring period so that every slot is a
+// constant; the tiles of a last, partial period run after the loop, each
+// under its own test, so no tile past KT is computed.
 // With U = 2D the refill during tile t is tile t+D-1, as in a stage ring; with
 // U = 5 (two and a half 64-deep stages of a 256 x 256 tile fit in 160 KB) the
 // refill is B(t+1) and A(t+2): B gets one tile of compute to land, A two.
@@ -51,8 +55,9 @@
 // barrier that frees it, and must be waited for at once (no overlap); it is
 // kept as the no-pipelining baseline.
 //
-// In every pipelined form the K loop is padded to a whole number of ring
-// periods with tiles whose loads are all out of range (they land as zeros).
+// The two-stage and whole-stage forms pad the K loop to a whole number of
+// ring periods with tiles whose loads are all out of range (they land as
+// zeros).
 #pragma once
 
 #if defined(__HIPCC__)

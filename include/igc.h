@@ -336,13 +336,13 @@ int64_t igc_pool_allocations(void);
  *            then MFMAs),
  *   kind 3 = workgroup barrier only (pipe_depth 1 frees its single stage with
  *            it; every schedule ends with one once nothing is left in flight).
- * The K loop is padded to a whole number of ring periods (U tiles for an odd
- * U, U/2 for an even one; no padding for pipe_depth 1) with tiles whose loads
- * are all out of range: they land as zeros and add nothing, so tiles up to
- * that padded count appear.  Rings of five or more slots issue units 0..U-3
- * up front and, during each tile t, units 2t+U-2 and 2t+U-1 (interleaved with
- * t's MFMAs) into the two slots the last barrier freed; units past the padded
- * count are issued out of range and never read.  Two-stage rings issue tile
+ * Rings of up to four slots pad the K loop to a whole number of ring periods
+ * (U/2 tiles; no padding for pipe_depth 1) with tiles whose loads are all out
+ * of range: they land as zeros and add nothing, so tiles up to that padded
+ * count appear.  Rings of five or more slots run exactly k_tiles tiles: they
+ * issue units 0..U-3 up front and, during each tile t, units 2t+U-2 and
+ * 2t+U-1 (interleaved with t's MFMAs) into the two slots the last barrier
+ * freed; units past k_tiles are issued out of range and never read.  Two-stage rings issue tile
  * t+2 right after the barrier that frees tile t.  Each wave drains its own
  * LDS reads before every barrier, so a barrier after a unit's reads frees its
  * slot.  (With ring_sync 1 the barrier of a wait event is replaced by the

@@ -298,7 +298,7 @@ def simulate_ring(D, KT, half=0):
     (unit 2t = A tile of K tile t, unit 2t+1 = its B tile) over U = 2D + half
     operand slots:
 
-    * every unit of the (padded) K loop is issued exactly once, into slot
+    * every unit of the K loop (padded for rings of up to four slots) is issued exactly once, into slot
       unit % U, and read exactly once; tiles are read in order;
     * a tile is read only after a wait for it, and that wait allows exactly the
       number of newer units this wave issued after the tile's B unit (loads
@@ -351,14 +351,17 @@ def simulate_ring(D, KT, half=0):
     KTp = KTp_of(D, half, KT)
     assert tiles_read == list(range(KTp))
     assert sorted(v for v in issued if v < 2 * KTp) == list(range(2 * KTp))
-    # spread rings also issue (out-of-range, never read) units past the padded loop
+    # spread rings also issue (out-of-range, never read) units past the last tile
     extra = [v for v in issued if v >= 2 * KTp]
     assert all(v < 2 * KTp + U - 2 for v in extra) and (U >= 5 or not extra)
 
 
 def KTp_of(D, half, KT):
+    """Tiles the K loop runs: whole ring periods for rings of up to four slots, exactly KT for spread rings."""
     U = 2 * D + half
-    period = 1 if D == 1 else (U if U % 2 else U // 2)
+    if U >= 5:
+        return KT
+    period = 1 if D == 1 else U // 2
     return -(-KT // period) * period
 
 
