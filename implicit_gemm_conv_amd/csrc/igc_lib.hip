@@ -665,8 +665,9 @@ int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chu
         if (chunks_per_row == 4) return logical_chunk ^ swz_k<4>(row);
         return -1;
     }
+    if (chunks_per_row == 8) return logical_chunk ^ swz_mn<8>(row);
     if (chunks_per_row < 16 || chunks_per_row % 16 != 0) return -1;
-    return logical_chunk ^ swz_mn(row);
+    return logical_chunk ^ swz_mn<16>(row);
 }
 
 int igc_stage_slot(int row, int slot, int slots_per_row) {

@@ -175,11 +175,24 @@ IGC_HD inline int swz_k(int row) {
         return (-(row >> 2)) & 3;  // 64-byte rows, four per 256 bytes
     }
 }
-// XOR swizzle of the 16-byte chunk index within an M/N-contiguous LDS row (at
-// least 16 chunks).  ds_read_b64_tr_b16 serves 32 lanes per phase; a 32x32x16
-// fragment read covers 4 k-rows x 4 chunks per phase, a 16x16x32 one 8 k-rows
-// (r and r+8, r = 0..3) x 2 chunks.
-IGC_HD inline int swz_mn(int row) { return 4 * (row & 3) + 2 * ((row >> 3) & 1); }
+// XOR swizzle of the 16-byte chunk index within an M/N-contiguous LDS row of
+// CPR chunks (8, or a multiple of 16).  ds_read_b64_tr_b16 serves 32 lanes per
+// phase; a 32x32x16 fragment read covers 4 k-rows x 4 chunks per phase, a
+// 16x16x32 one 8 k-rows (r and r+8, r = 0..3) x 2 chunks.  Rows of 256 bytes
+// or more all start on bank 0, so the 8 k-rows of a phase need 8 distinct
+// chunk pairs (and quads), which 4*(r&3) + 2*bit3 gives.  Rows of 128 bytes
+// alternate between the two halves of the 64 banks, so only rows of equal
+// parity compete: 4*bit1 + 2*bit3 separates rows 0, 2, 8 and 10 (and 1, 3, 9,
+// 11) into distinct pairs and rows 0 and 2 into distinct quads.  Both maps use
+// bits 0, 1 and 3 of the row only and stay inside the row.
+template <int CPR>
+IGC_HD inline int swz_mn(int row) {
+    static_assert(CPR == 8 || CPR % 16 == 0, "M/N-contiguous rows of 64 elements or a multiple of 128");
+    if constexpr (CPR == 8)
+        return 4 * ((row >> 1) & 1) + 2 * ((row >> 3) & 1);
+    else
+        return 4 * (row & 3) + 2 * ((row >> 3) & 1);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords, kRsrcFlags);
@@ -254,7 +267,7 @@ struct Tile {
         if constexpr (KC) {
             return (lane % CPR) ^ swz_k<CPR>(row);
         } else {
-            return (lane % CPR) ^ swz_mn(row);
+            return (lane % CPR) ^ swz_mn<CPR>(row);
         }
     }
 };
@@ -489,17 +502,17 @@ struct Mainloop {
         const int g = lane >> 4, i16 = lane & 15;
         const int mn_rowpart = MI == 32 ? 8 * (g >> 1) + (i16 >> 2) : 8 * g + (i16 >> 2);
         const int mn_u = MI == 32 ? 2 * (g & 1) + ((i16 & 3) >> 1) : ((i16 & 3) >> 1);
-        const int mn_s = swz_mn(mn_rowpart);
         if constexpr (C::A_KC) {
             const int row = wm * C::WTM + (lane % MI);
             const int x = (lane / MI) ^ swz_k<TA::CPR>(row);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) fa_off[kk] = row * BK * 2 + (((NH * kk) ^ x) * 16);
         } else {
+            const int mn_sa = swz_mn<TA::CPR>(mn_rowpart);
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int cl = (wm * C::WTM) / 8 + (MI / 8) * i + mn_u;
-                fa_off[i] = mn_rowpart * BM * 2 + ((cl ^ mn_s) * 16) + 8 * (i16 & 1);
+                fa_off[i] = mn_rowpart * BM * 2 + ((cl ^ mn_sa) * 16) + 8 * (i16 & 1);
             }
         }
         if constexpr (C::B_KC) {
@@ -508,10 +521,11 @@ struct Mainloop {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) fb_off[kk] = row * BK * 2 + (((NH * kk) ^ x) * 16);
         } else {
+            const int mn_sb = swz_mn<TB::CPR>(mn_rowpart);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int cl = (wn * C::WTN) / 8 + (MI / 8) * j + mn_u;
-                fb_off[j] = mn_rowpart * BN * 2 + ((cl ^ mn_s) * 16) + 8 * (i16 & 1);
+                fb_off[j] = mn_rowpart * BN * 2 + ((cl ^ mn_sb) * 16) + 8 * (i16 & 1);
             }
         }
     }

@@ -81,6 +81,20 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op) {
         }
         return big;
     }
+    // A forward convolution with a shallow K (a 1x1 filter, or few channels)
+    // is bound by load latency rather than by the MFMAs: 64-column tiles in a
+    // two-stage ring take 48 KB (128 rows, 4 waves) or 80 KB (256 rows, 8
+    // waves) of LDS, so three or two workgroups share a CU and keep more loads
+    // in flight.  Measured: the 1x1 workload (K = 64 outputs, C = 256) 38 ->
+    // 19 us with 256 rows (20 us with 128), the C = 96, K = 192 3x3 workload
+    // 30 -> 24 us with 128 rows (25 us with 256); a deep K (the 27 x 27 3x3
+    // workload, C = 256) is slower with them (32-34 us against 25).
+    if (op == IGC_OP_CONV_FPROP && K <= 1024 && N <= 256) {
+        const igc_tune_t narrow = N <= 64 ? igc_tune_t{256, 64, 64, 2, 8, 16, 0, 4, 1, 0, 0, 0}
+                                          : igc_tune_t{128, 64, 64, 2, 4, 16, 0, 0, 1, 0, 0, 0};
+        const Instance* e = find_instance(narrow, false, true, true, IGC_OP_CONV_FPROP);
+        if (e && e->full) return narrow;
+    }
     // Small tiles.  When even they leave CUs idle and K is deep (at least 2048
     // per CU's share), the K work is spread over every CU: a 2-way split when
     // the tiles fill exactly half the CUs (each workgroup one half of a tile,

@@ -18,6 +18,8 @@
 #define IGC_FOR_EACH_TILE(X)                  \
     X(256, 256, 64, 2, 8, 16, 1, 4, 0, 3)     \
     X(224, 256, 64, 2, 8, 16, 1, 4, 0, 4)     \
+    X(128, 64, 64, 2, 4, 16, 0, 0, 0, 4)      \
+    X(256, 64, 64, 2, 8, 16, 0, 4, 0, 4)      \
     X(128, 128, 64, 4, 8, 16, 0, 4, 0, 3)     \
     X(256, 256, 32, 4, 8, 16, 0, 4, 0, 3)     \
     X(128, 128, 64, 4, 4, 32, 0, 0, 0, 2)     \

@@ -361,7 +361,7 @@ int igc_ring_schedule(int pipe_depth, int half_stage, int k_tiles, int *events, 
  * logical chunk `logical_chunk` of row `row` is stored at the returned
  * physical chunk of the same row.  k_contiguous = 1: rows of the K tile
  * (chunks_per_row = BK/8, 8 or 4); 0: rows of BM or BN elements read with the
- * transposing LDS load (chunks_per_row a multiple of 16).  Returns -1 for an
+ * transposing LDS load (chunks_per_row 8 or a multiple of 16).  Returns -1 for an
  * unsupported geometry.  These are the maps the kernels use.
  */
 int igc_lds_chunk(int k_contiguous, int chunks_per_row, int row, int logical_chunk);

@@ -212,7 +212,7 @@ def test_tune_table_fits_lds():
     assert set(igc.tunes(igc.SCOPE_ALL | igc.SCOPE_STREAM_K)) >= {(256, 256, 64, 2, 8, 16, 1, 4, 0),
                                                                   (256, 256, 32, 4, 8, 16, 0, 4, 0),
                                                                   (128, 128, 64, 4, 8, 16, 0, 4, 0)}
-    assert C224 in igc.tunes(igc.SCOPE_CONV_FPROP)
+    assert {C224, N256, N128} <= set(igc.tunes(igc.SCOPE_CONV_FPROP))
     for (bm, bn, bk, d, w, mi, h, lw, sy) in tunes:
         assert 1 <= lw <= w and w % lw == 0
         lds = igc.igc_tune_lds_bytes((bm, bn, bk, d, w, mi, h, lw, sy))
@@ -235,6 +235,8 @@ T25 = (256, 256, 64, 2, 8, 16, 1, 4, 0)   # 256 x 256 x 64, two and a half stage
 BIG = (256, 256, 32, 4, 8, 16, 0, 4, 0)   # 256 x 256 x 32, four stages: data gradient
 S8 = (128, 128, 64, 4, 8, 16, 0, 4, 0)    # 128 x 128 x 64, 8 waves: small grids
 C224 = (224, 256, 64, 2, 8, 16, 1, 4, 0)  # 224 x 256 x 64: forward convolutions whose 256-row tiles fill rounds badly
+N256 = (256, 64, 64, 2, 8, 16, 0, 4, 0)   # 64-column tiles, two stages: shallow forward convolutions,
+N128 = (128, 64, 64, 2, 4, 16, 0, 4, 0)   # two or three workgroups per CU
 
 
 @pytest.mark.parametrize("shape,op,expect", [
@@ -253,7 +255,10 @@ C224 = (224, 256, 64, 2, 8, 16, 1, 4, 0)  # 224 x 256 x 64: forward convolutions
     ((1000, 1000, 65536), igc.OP_CONV_FPROP, (S8, 1, 256, 0)),       # (a forward conv view stays stream-K)
     ((1000, 512, 8192), igc.OP_GEMM, (S8, 1, 256, 0)),               # 8 big tiles: 32 splits of 256 are too short
     ((1000, 1000, 3000), igc.OP_GEMM, (S8, 1, 0, 0)),                # too little K to share
-    ((100352, 64, 256), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),           # 1x1 conv with 64 outputs: 128-wide tiles
+    ((100352, 64, 256), igc.OP_CONV_FPROP, (N256, 1, 0, 0)),         # 1x1 conv with 64 outputs: shallow K
+    ((25088, 192, 864), igc.OP_CONV_FPROP, (N128, 1, 0, 0)),         # 3x3 conv with C = 96, K = 192: shallow K
+    ((25088, 320, 864), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),           # ... but more than 256 outputs
+    ((100352, 64, 256), igc.OP_GEMM, (S8, 1, 0, 0)),                 # (a GEMM keeps the 128 x 128 tiles)
     ((11664, 256, 2304), igc.OP_CONV_FPROP, (S8, 1, 0, 0)),          # 27x27 images: 46 big tiles vs 184 small
     ((128, 96, 200), igc.OP_GEMM, (S8, 1, 0, 0)),
     ((0, 5, 7), igc.OP_GEMM, (S8, 1, 0, 0)),

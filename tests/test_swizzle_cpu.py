@@ -32,7 +32,7 @@ def chunk(kc, cpr, row, c):
     return L.igc_lds_chunk(kc, cpr, row, c)
 
 
-@pytest.mark.parametrize("kc,cpr", [(1, 8), (1, 4), (0, 16), (0, 32)])
+@pytest.mark.parametrize("kc,cpr", [(1, 8), (1, 4), (0, 8), (0, 16), (0, 32)])
 def test_swizzle_is_a_permutation_per_row(kc, cpr):
     for row in range(64):
         phys = [chunk(kc, cpr, row, c) for c in range(cpr)]
@@ -99,7 +99,7 @@ def test_bank_model_rejects_the_measured_conflicting_map():
 
 
 @pytest.mark.parametrize("mi", [32, 16])
-@pytest.mark.parametrize("rows_elems", [256, 128])
+@pytest.mark.parametrize("rows_elems", [256, 128, 64])
 def test_mn_contiguous_transposed_reads_conflict_free(rows_elems, mi):
     """ds_read_b64_tr_b16 (32 lanes per phase, 8 bytes each): in 16-lane group G, lane i reads 8 bytes at
     element column 4*(i%4) of its group's 16 columns, k-row i//4 of its group's 4 rows (plus 4 for the second
@@ -126,6 +126,14 @@ def test_mn_contiguous_transposed_reads_conflict_free(rows_elems, mi):
                 for g0 in range(0, 64, group):
                     units = bank_units(addrs[g0:g0 + group], 8, window)
                     assert len(set(units)) == group, (rows_elems, mi, frag, kk, h, g0)
+
+
+def test_wide_row_mn_map_does_not_fit_64_element_rows():
+    """The map for rows of 128+ elements XORs up to 14 into the chunk index: on 8-chunk rows it would leave the
+    row, so 64-element rows need their own map (the 128-byte row pitch already separates odd and even rows)."""
+    wide = lambda r: 4 * (r & 3) + 2 * ((r >> 3) & 1)
+    assert any((c ^ wide(r)) >= 8 for r in range(16) for c in range(8))
+    assert all(0 <= chunk(0, 8, r, c) < 8 for r in range(64) for c in range(8))
 
 
 def test_old_mn_map_conflicts_for_16x16x32():
@@ -203,7 +211,8 @@ def test_old_staging_map_conflicts():
 
 def test_unsupported_geometry():
     assert chunk(1, 16, 0, 0) == -1
-    assert chunk(0, 8, 0, 0) == -1
+    assert chunk(0, 4, 0, 0) == -1 and chunk(0, 24, 0, 0) == -1
+    assert chunk(0, 8, 0, 8) == -1
     assert chunk(1, 8, 0, 8) == -1
     assert stage_slot(-1, 0, 16) == -1 and stage_slot(0, -1, 16) == -1
     assert stage_slot(0, 16, 16) == -1 and stage_slot(0, 0, 8) == -1
