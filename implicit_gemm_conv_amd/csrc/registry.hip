@@ -96,26 +96,31 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op) {
         if (e && e->full) return narrow;
     }
     // Small tiles.  When even they leave CUs idle and K is deep (at least 2048
-    // per CU's share), the K work is spread over every CU: a 2-way split when
-    // the tiles fill exactly half the CUs (each workgroup one half of a tile,
-    // summed by the reduction kernel), stream-K otherwise (measured: 2-way
-    // split 79 us vs stream-K 82-87 us on 2048 x 1024 x 16384; stream-K 176 us
-    // vs a 4-way split 194 us on 1000 x 1000 x 65536).
+    // per workgroup), the K work is spread over every CU.  An even K split
+    // into S = CUs / tiles parts is taken when it fills at least 7/8 of the
+    // CUs (each workgroup one part of a tile, the fp32 partials summed in
+    // split order by the reduction kernel): it beats stream-K, whose runs
+    // cross tile boundaries and make owners wait on other workgroups
+    // (measured: 2048 x 1024 x 16384 2-way 75-80 us vs stream-K 82-87; the
+    // filter gradient of the 3x3 workload, 36 tiles, 7-way 154-157 us vs
+    // 182-185; 1000 x 1000 x 65536 4-way 167-171 vs 178-180).  Otherwise
+    // stream-K over every CU.
     if (t128 > 0 && t128 < kCUs && K / 2048 >= 2) {
-        if (t128 * 2 == kCUs) {
-            small.k_splits = 2;
-        } else {
-            // A GEMM whose 256 x 256 tiles divide the CUs evenly into K splits of at least 2048 runs those
-            // (the partials are summed by the reduction kernel; measured on 1000 x 1000 x 65536: 16 splits
-            // 168-177 us against 186-190 for 128 x 128 stream-K); otherwise stream-K over every CU.
-            const int64_t S = t256 > 0 ? kCUs / t256 : 0;
-            if (op == IGC_OP_GEMM && S >= 2 && S * t256 == kCUs && K / S >= 2048) {
-                igc_tune_t t = {256, 256, 64, 2, 8, 16, 1, 4, 1, 0, 0, 0};
-                t.k_splits = (int)S;
-                return t;
-            }
-            small.stream_k = (int)kCUs;
+        // A GEMM whose 256 x 256 tiles divide the CUs evenly into K splits of at least 4096 runs those
+        // (measured on 1000 x 1000 x 65536: 16 splits 163-164 us against 167-171 for a 4-way split of the
+        // 128 x 128 tiles; with 2048 per split, on 2048 x 1024 x 16384, 8 splits of the big tiles lose
+        // to 2 of the small ones, 82-84 us against 75-80).
+        const int64_t S = t256 > 0 ? kCUs / t256 : 0;
+        if (op == IGC_OP_GEMM && S >= 2 && S * t256 == kCUs && K / S >= 4096) {
+            igc_tune_t t = {256, 256, 64, 2, 8, 16, 1, 4, 1, 0, 0, 0};
+            t.k_splits = (int)S;
+            return t;
         }
+        const int64_t s128 = kCUs / t128;
+        if (s128 >= 2 && s128 * t128 * 8 >= kCUs * 7 && K / s128 >= 2048)
+            small.k_splits = (int)s128;
+        else
+            small.stream_k = (int)kCUs;
     }
     return small;
 }

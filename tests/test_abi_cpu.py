@@ -249,10 +249,13 @@ N128 = (128, 64, 64, 2, 4, 16, 0, 4, 0)   # two or three workgroups per CU
                                                                      # 784 small ones (4 rounds); 224 of 224 rows
                                                                      # still make one round, of 7/8 the work
     ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
-    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (S8, 1, 256, 0)),       # the conv's filter gradient: 36 tiles, deep K
+    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (S8, 7, 0, 0)),         # the conv's filter gradient: 36 tiles x 7 splits
     ((2048, 1024, 16384), igc.OP_GEMM, (S8, 2, 0, 0)),               # 128 tiles of 128x128 = half the CUs: 2-way split
     ((1000, 1000, 65536), igc.OP_GEMM, (T25, 16, 0, 0)),             # 16 big tiles split 16 ways fill the CUs
-    ((1000, 1000, 65536), igc.OP_CONV_FPROP, (S8, 1, 256, 0)),       # (a forward conv view stays stream-K)
+    ((1000, 1000, 65536), igc.OP_CONV_FPROP, (S8, 4, 0, 0)),         # (a forward conv view: 64 tiles x 4 splits)
+    ((1000, 1200, 65536), igc.OP_CONV_FPROP, (S8, 3, 0, 0)),         # 80 tiles x 3 = 240 CUs, over 7/8 of 256
+    ((1000, 1300, 65536), igc.OP_CONV_FPROP, (S8, 1, 256, 0)),       # 88 tiles x 2 = 176 CUs: stream-K instead
+
     ((1000, 512, 8192), igc.OP_GEMM, (S8, 1, 256, 0)),               # 8 big tiles: 32 splits of 256 are too short
     ((1000, 1000, 3000), igc.OP_GEMM, (S8, 1, 0, 0)),                # too little K to share
     ((100352, 64, 256), igc.OP_CONV_FPROP, (N256, 1, 0, 0)),         # 1x1 conv with 64 outputs: shallow K

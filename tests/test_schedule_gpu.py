@@ -118,10 +118,11 @@ def test_conv_caller_workspace():
 
 
 def test_stream_k_graph_replay():
-    """A built-in stream-K call (1024 x 1024 x 8192: 64 tiles of 128 x 128 over 256 workgroups) captured in a
-    HIP graph with a caller workspace, replayed with new inputs each time, eager work and synchronisation between
-    replays: every replay equals the eager call on the same inputs bit for bit."""
-    M, N, K = 1024, 1024, 8192
+    """A built-in stream-K call (1024 x 1024 x 4096: 64 tiles of 128 x 128 over 256 workgroups; a 4-way split
+    would leave 1024 of K per split) captured in a HIP graph with a caller workspace, replayed with new inputs
+    each time, eager work and synchronisation between replays: every replay equals the eager call on the same
+    inputs bit for bit."""
+    M, N, K = 1024, 1024, 4096
     t = igc.igc_default_tune(M, N, K)
     assert t.stream_k > 0
     need = igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K)
