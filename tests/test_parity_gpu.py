@@ -458,17 +458,24 @@ CONV_CASES = [
 ]
 
 
+# Besides the built-in tile (64-column tiles for these shallow filters), every case also runs on the 128 x 128
+# tile and the 128 x 64 one, so each loop variant is checked on square and narrow tiles.
+CONV_VARIANT_TUNES = [(128, 128, 64, 4, 8, 16, 0, 4, 0), (128, 64, 64, 2, 4, 16, 0, 4, 0)]
+
+
 @pytest.mark.parametrize("case", CONV_CASES)
 def test_conv_variants(case):
     N, H, W, C, K, R, S, sh, sw, ph, pw, dh, dw = case
     geo = dict(sh=sh, sw=sw, ph=ph, pw=pw, dh=dh, dw=dw)
+    tunes = [None] + [t for t in CONV_VARIANT_TUNES if t in FPROP_TUNES | FULL_TUNES]
     for i, (dtype, out) in enumerate((("bf16", "f32"), ("fp16", "f16"), ("bf16", "bf16"))):
         x, w = inputs.conv_operands(N, H, W, C, K, R, S, dtype, ("normal", 1.0), ("normal", 0.1), seed=31 + i)
-        say(f"conv {case} {dtype}->{out}")
-        y, _ = run_conv(N, H, W, C, K, R, S, x, w, out=out, dtype=dtype, **geo)
         ref, Sabs = oracle.conv2d_nhwc(N, H, W, C, K, R, S, x, w, oracle.FP16 if dtype == "fp16" else oracle.BF16,
                                        **geo)
-        assert_close(y, ref, Sabs, out, f"conv {case} {dtype}->{out}")
+        for tune in tunes:
+            say(f"conv {case} {dtype}->{out} tune={tune}")
+            y, _ = run_conv(N, H, W, C, K, R, S, x, w, out=out, dtype=dtype, tune=tune, **geo)
+            assert_close(y, ref, Sabs, out, f"conv {case} {dtype}->{out} tune={tune}")
 
 
 @pytest.mark.parametrize("tune", ALL_TUNES, ids=[",".join(map(str, t)) for t in ALL_TUNES])
