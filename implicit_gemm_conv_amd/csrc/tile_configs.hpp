@@ -22,8 +22,8 @@
     X(256, 64, 64, 2, 8, 16, 0, 4, 0, 4)      \
     X(128, 128, 64, 4, 8, 16, 0, 4, 0, 3)     \
     X(256, 256, 32, 4, 8, 16, 0, 4, 0, 3)     \
-    X(128, 128, 64, 4, 4, 32, 0, 0, 0, 2)     \
-    X(256, 128, 64, 3, 8, 16, 0, 4, 0, 2)     \
+    X(128, 128, 64, 4, 4, 32, 0, 0, 0, 3)     \
+    X(256, 128, 64, 3, 8, 16, 0, 4, 0, 3)     \
     X(256, 256, 32, 2, 8, 32, 0, 4, 0, 0)     \
     X(256, 256, 32, 3, 8, 32, 0, 4, 0, 0)     \
     X(256, 256, 32, 4, 8, 32, 0, 4, 0, 0)     \

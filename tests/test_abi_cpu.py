@@ -234,6 +234,7 @@ def test_tune_table_fits_lds():
 T25 = (256, 256, 64, 2, 8, 16, 1, 4, 0)   # 256 x 256 x 64, two and a half stages: GEMM and forward convolution
 BIG = (256, 256, 32, 4, 8, 16, 0, 4, 0)   # 256 x 256 x 32, four stages: data gradient
 S8 = (128, 128, 64, 4, 8, 16, 0, 4, 0)    # 128 x 128 x 64, 8 waves: small grids
+R8 = (256, 128, 64, 3, 8, 16, 0, 4, 0)    # 256 x 128 x 64, three stages: the filter gradient's K split
 C224 = (224, 256, 64, 2, 8, 16, 1, 4, 0)  # 224 x 256 x 64: forward convolutions whose 256-row tiles fill rounds badly
 N256 = (256, 64, 64, 2, 8, 16, 0, 4, 0)   # 64-column tiles, two stages: shallow forward convolutions,
 N128 = (128, 64, 64, 2, 4, 16, 0, 4, 0)   # two or three workgroups per CU
@@ -249,7 +250,8 @@ N128 = (128, 64, 64, 2, 4, 16, 0, 4, 0)   # two or three workgroups per CU
                                                                      # 784 small ones (4 rounds); 224 of 224 rows
                                                                      # still make one round, of 7/8 the work
     ((256 * 255, 256 * 5, 2304), igc.OP_GEMM, (T25, 1, 0, 0)),
-    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (S8, 7, 0, 0)),         # the conv's filter gradient: 36 tiles x 7 splits
+    ((256, 2304, 100352), igc.OP_CONV_WGRAD, (R8, 14, 0, 0)),        # the conv's filter gradient: 18 tiles x 14 splits
+    ((256, 2304, 100352), igc.OP_GEMM, (S8, 7, 0, 0)),               # (as a GEMM: 36 tiles of 128 x 128, 7 splits)
     ((2048, 1024, 16384), igc.OP_GEMM, (S8, 2, 0, 0)),               # 128 tiles of 128x128 = half the CUs: 2-way split
     ((1000, 1000, 65536), igc.OP_GEMM, (T25, 16, 0, 0)),             # 16 big tiles split 16 ways fill the CUs
     ((1000, 1000, 65536), igc.OP_CONV_FPROP, (S8, 4, 0, 0)),         # (a forward conv view: 64 tiles x 4 splits)

@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 # the configurations built for every operation
 T25, BIG, S8 = (256, 256, 64, 2, 8, 16, 1, 4, 0), (256, 256, 32, 4, 8, 16, 0, 4, 0), (128, 128, 64, 4, 8, 16, 0, 4, 0)
+R8 = (256, 128, 64, 3, 8, 16, 0, 4, 0)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -79,7 +80,8 @@ def test_wgrad(case):
         dy = inputs.draw(N * P * Q * K, ("normal", 1.0), dtype, gen).reshape(N, P, Q, K)
         ref, Sabs = oracle.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, x, dy, oracle.FP16 if dtype == "fp16" else
                                              oracle.BF16, **geo)
-        for tune in (None, S8, BIG, T25, igc.tune(S8, k_splits=3), igc.tune(BIG, stream_k=5)):
+        for tune in (None, S8, BIG, T25, R8, igc.tune(S8, k_splits=3), igc.tune(R8, k_splits=4),
+                     igc.tune(BIG, stream_k=5)):
             say(f"wgrad {case} {dtype}->{out} tune={tune}")
             y, _ = run_conv(N, H, W, C, K, R, S, x, dy, out=out, dtype=dtype, tune=tune, op="wgrad", **geo)
             assert_close(y, ref, Sabs, out, f"wgrad {case} {dtype}->{out} tune={tune}")
@@ -103,7 +105,8 @@ def test_grads_exact_integers(op, out):
     else:
         ref, _ = oracle.conv2d_wgrad_nhwc(N, H, W, C, K, R, S, x, dy, oracle.BF16, **geo)
         args = (x, dy)
-    for tune in (None, S8, BIG, T25, igc.tune(BIG, k_splits=2), igc.tune(S8, stream_k=7)):
+    for tune in (None, S8, BIG, T25, R8, igc.tune(BIG, k_splits=2), igc.tune(R8, k_splits=3),
+                 igc.tune(S8, stream_k=7)):
         say(f"exact {op} -> {out} tune={tune}")
         y, _ = run_conv(N, H, W, C, K, R, S, *args, out=out, tune=tune, op=op, **geo)
         bad = np.count_nonzero(y != round_to(ref, out))
