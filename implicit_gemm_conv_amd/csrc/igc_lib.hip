@@ -570,7 +570,7 @@ igc_status_t gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, i
                                const void* B, int64_t ldb, igc_layout_t lb, void* C, int64_t ldc, igc_out_t c_type,
                                igc_stream_t stream) {
     // the built-in schedule, with its workspace in this device's scratch array;
-    // when that schedule needs more (a K split of 256 x 256 tiles), 128 x 128
+    // when that schedule needs more (a K split of 256 x 128 tiles), 128 x 128
     // stream-K over 256 workgroups, whose workspace always fits
     if (M < 0 || N < 0 || K < 0) return IGC_ERR_INVALID_VALUE;
     const bool a_kc = la == IGC_ROW_MAJOR, b_kc = lb == IGC_COL_MAJOR;

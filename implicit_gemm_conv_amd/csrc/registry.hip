@@ -106,24 +106,21 @@ igc_tune_t default_tune(int64_t M, int64_t N, int64_t K, int op) {
     // 182-185; 1000 x 1000 x 65536 4-way 167-171 vs 178-180).  Otherwise
     // stream-K over every CU.
     if (t128 > 0 && t128 < kCUs && K / 2048 >= 2) {
-        // A GEMM whose 256 x 256 tiles divide the CUs evenly into K splits of at least 4096 runs those
-        // (measured on 1000 x 1000 x 65536: 16 splits 163-164 us against 167-171 for a 4-way split of the
-        // 128 x 128 tiles; with 2048 per split, on 2048 x 1024 x 16384, 8 splits of the big tiles lose
-        // to 2 of the small ones, 82-84 us against 75-80).
-        const int64_t S = t256 > 0 ? kCUs / t256 : 0;
-        if (op == IGC_OP_GEMM && S >= 2 && S * t256 == kCUs && K / S >= 4096) {
-            igc_tune_t t = {256, 256, 64, 2, 8, 16, 1, 4, 1, 0, 0, 0};
-            t.k_splits = (int)S;
-            return t;
-        }
-        // The filter gradient reads both operands with transposing LDS loads, so the 256 x 128 tile's
-        // larger wave sub-tile (128 x 32 against 64 x 32) pays: its 18 tiles on the 3x3 workload split
-        // 14 ways ran 130-140 us against 160-192 for 128 x 128 tiles split 7 ways.
-        if (op == IGC_OP_CONV_WGRAD) {
+        // 256 x 128 tiles (three stages, wave sub-tiles of 128 x 32 against 64 x 32 for 128 x 128 tiles:
+        // fewer LDS bytes per flop) split S ways, when that fills at least 7/8 of the CUs and leaves each
+        // part 8192 or more of K.  Measured on 1000 x 1000 x 65536: 8 parts 151-163 us, against 158-185
+        // for 16 parts of 256 x 256 tiles and 167-173 for 4 parts of 128 x 128; with 4096 per part
+        // (2048 x 1024 x 16384: 4 parts) it only ties the 128 x 128 2-way split while doubling the partial
+        // sums.  The filter gradient, whose operands both take transposing LDS reads, gains more and takes
+        // it down to 2048 per part (the 3x3 workload's 18 tiles: 14 parts, 130-141 us against 154-192 for
+        // 7 parts of 128 x 128).
+        {
             igc_tune_t r = {256, 128, 64, 3, 8, 16, 0, 4, 1, 0, 0, 0};
             const int64_t tr = ((M + 255) / 256) * ((N + 127) / 128), sr = tr > 0 ? kCUs / tr : 0;
-            const Instance* e = find_instance(r, false, false, false, IGC_OP_CONV_WGRAD);
-            if (e && e->full && sr >= 2 && sr * tr * 8 >= kCUs * 7 && K / sr >= 2048) {
+            const int64_t kmin = op == IGC_OP_CONV_WGRAD ? 2048 : 8192;
+            const bool a_kc = op != IGC_OP_CONV_WGRAD, b_kc = op == IGC_OP_CONV_FPROP;
+            const Instance* e = find_instance(r, false, a_kc, b_kc, op);
+            if (e && e->full && sr >= 2 && sr * tr * 8 >= kCUs * 7 && K / sr >= kmin) {
                 r.k_splits = (int)sr;
                 return r;
             }

@@ -261,7 +261,7 @@ igc_status_t conv2d_nhwc_wgrad_implicit_gemm_fp16_ex(int N, int H, int W, int C,
  * in a library-owned device array of 16 MiB + 4 KiB that each GPU holds until
  * the process ends.  The call allocates nothing.  When the built-in schedule's
  * workspace fits the array it runs that schedule and gives the same bits as
- * gemm_bf16; otherwise (a K split of 256 x 256 tiles, e.g. 1024 x 1024 x 65536)
+ * gemm_bf16; otherwise (a K split of 256 x 128 tiles, e.g. 1024 x 1024 x 65536)
  * it runs 128 x 128 stream-K over 256 workgroups, whose workspace always fits,
  * with a different summation order.  Calls that overlap on one GPU share the
  * array and race: order them (one stream).  IGC_ERR_HIP if the array cannot

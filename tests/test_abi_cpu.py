@@ -253,9 +253,11 @@ N128 = (128, 64, 64, 2, 4, 16, 0, 4, 0)   # two or three workgroups per CU
     ((256, 2304, 100352), igc.OP_CONV_WGRAD, (R8, 14, 0, 0)),        # the conv's filter gradient: 18 tiles x 14 splits
     ((256, 2304, 100352), igc.OP_GEMM, (S8, 7, 0, 0)),               # (as a GEMM: 36 tiles of 128 x 128, 7 splits)
     ((2048, 1024, 16384), igc.OP_GEMM, (S8, 2, 0, 0)),               # 128 tiles of 128x128 = half the CUs: 2-way split
-    ((1000, 1000, 65536), igc.OP_GEMM, (T25, 16, 0, 0)),             # 16 big tiles split 16 ways fill the CUs
-    ((1000, 1000, 65536), igc.OP_CONV_FPROP, (S8, 4, 0, 0)),         # (a forward conv view: 64 tiles x 4 splits)
-    ((1000, 1200, 65536), igc.OP_CONV_FPROP, (S8, 3, 0, 0)),         # 80 tiles x 3 = 240 CUs, over 7/8 of 256
+    ((1000, 1000, 65536), igc.OP_GEMM, (R8, 8, 0, 0)),               # 32 tiles of 256 x 128 split 8 ways
+    ((1000, 1000, 65536), igc.OP_CONV_FPROP, (R8, 8, 0, 0)),         # (the same as a forward conv view)
+    ((1000, 1000, 32768), igc.OP_GEMM, (S8, 4, 0, 0)),               # 4096 per part is too short for 256 x 128
+    ((1000, 1200, 65536), igc.OP_CONV_FPROP, (R8, 6, 0, 0)),         # 40 tiles x 6 = 240 CUs, over 7/8 of 256
+    ((1000, 1200, 32768), igc.OP_CONV_FPROP, (S8, 3, 0, 0)),         # 5461 per part: 128 x 128 tiles, 80 x 3
     ((1000, 1300, 65536), igc.OP_CONV_FPROP, (S8, 1, 256, 0)),       # 88 tiles x 2 = 176 CUs: stream-K instead
 
     ((1000, 512, 8192), igc.OP_GEMM, (S8, 1, 256, 0)),               # 8 big tiles: 32 splits of 256 are too short
@@ -281,7 +283,7 @@ def test_workspace_bytes():
     assert ws(igc.OP_GEMM, 8192, 8192, 8192) == 0
     assert ws(igc.OP_CONV_FPROP, 100352, 256, 2304) == 0
     assert ws(igc.OP_GEMM, 2048, 1024, 16384) == 2 * 2048 * 1024 * 4
-    assert ws(igc.OP_GEMM, 1000, 1000, 65536) == 16 * 1000 * 1000 * 4     # built-in: 256 x 256 tiles split 16
+    assert ws(igc.OP_GEMM, 1000, 1000, 65536) == 8 * 1000 * 1000 * 4      # built-in: 256 x 128 tiles split 8
     assert ws(igc.OP_GEMM, 1000, 512, 8192) == 256 * 128 * 128 * 4 + 1024  # built-in: stream-K over 256
     assert ws(igc.OP_GEMM, 1000, 1000, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4
     assert ws(igc.OP_GEMM, 1000, 998, 6144, (128, 128, 64, 4, 4, 32, 0, 4, 4, 0)) == 4 * 1000 * 1000 * 4

@@ -50,12 +50,12 @@ def test_noalloc_matches_gemm_bf16():
 
 
 def test_noalloc_falls_back_to_stream_k():
-    """A shape whose built-in schedule (16-way split of 256 x 256 tiles, 64 MiB of partials) outgrows the
+    """A shape whose built-in schedule (8-way split of 256 x 128 tiles, 32 MiB of partials) outgrows the
     array: the no-allocation call runs 128 x 128 stream-K over 256 workgroups instead, equal bit for bit to
     that schedule run with a caller workspace, within the oracle's bound, and allocates nothing."""
     M, N, K = 1024, 1024, 65536
     t = igc.igc_default_tune(M, N, K)
-    assert t.k_splits == 16 and igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K) > (16 << 20) + 4096
+    assert t.k_splits == 8 and igc.igc_workspace_bytes(igc.OP_GEMM, M, N, K) > (16 << 20) + 4096
     fits = igc.tune((128, 128, 64, 4, 8, 16, 0, 4, 0), stream_k=256)
     A, lda, B, ldb = inputs.gemm_operands(M, N, K, "row", "row", dtype="bf16", a_dist=("normal", 1.0),
                                           b_dist=("normal", 1.0), seed=17)
