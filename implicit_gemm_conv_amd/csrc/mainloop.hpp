@@ -183,8 +183,8 @@ IGC_HD inline int swz_k(int row) {
 // chunk pairs (and quads), which 4*(r&3) + 2*bit3 gives.  Rows of 128 bytes
 // alternate between the two halves of the 64 banks, so only rows of equal
 // parity compete: 4*bit1 + 2*bit3 separates rows 0, 2, 8 and 10 (and 1, 3, 9,
-// 11) into distinct pairs and rows 0 and 2 into distinct quads.  Both maps use
-// bits 0, 1 and 3 of the row only and stay inside the row.
+// 11) into distinct pairs and rows 0 and 2 into distinct quads.  Neither map
+// uses a row bit other than 0, 1 and 3, and both stay inside the row.
 template <int CPR>
 IGC_HD inline int swz_mn(int row) {
     static_assert(CPR == 8 || CPR % 16 == 0, "M/N-contiguous rows of 64 elements or a multiple of 128");
@@ -1268,51 +1268,51 @@ __device__ __forceinline__ void run_tile_as(const Params p, int tm, int tn, int6
         ml.read_frags(slot_a<C, 0>(), slot_b<C, 0>(), 0, fa[0], fb[0]);
         // Tile t0+u of a period (u a constant, so every slot is one).
         auto tile = [&](auto UU, const int t0) __attribute__((always_inline)) {
-                constexpr int u = UU;
-                const int t = t0 + u;
-                // the two units refilled during tile t
-                constexpr int s1 = 2 * u + U - 2, s2 = 2 * u + U - 1;
-                constexpr int op1 = s1 % 2, op2 = s2 % 2;
-                const int t1 = t + (U - 2 - op1) / 2, t2 = t + (U - 1 - op2) / 2;
-                IGC_LDS char* d1 = slot<C, Ring::slot_of(U, s1)>();
-                IGC_LDS char* d2 = slot<C, Ring::slot_of(U, s2)>();
-                constexpr int p0 = (u * KK) & 1;  // fragment set of this tile's k-step 0
-                if constexpr (CTR && LOADER) {
-                    // the refill goes into the stage of tile t-1 (pass (t-1)/D, P == D here): every
-                    // wave must be done reading it; nothing to wait for before tile 0
-                    constexpr int sf = (u + D - 1) % D;
-                    late |= wait_count(ctr + D + sf, C::NW * (t0 / D + (u >= 1 ? 1 : 0)));
-                }
-                // k-steps 0 .. KK-2: refill, read ahead, MFMA
-                static_for<0, KK - 1>([&](auto KI) __attribute__((always_inline)) {
-                    constexpr int kk = KI;
-                    constexpr int pc = (p0 + kk) & 1, pn = pc ^ 1;
-                    ml.template issue_units_part<kk, KK, op1, op2>(t1, d1, t2, d2);
-                    ml.read_frags(slot_a<C, u>(), slot_b<C, u>(), kk + 1, fa[pn], fb[pn]);
-                    ML::mma(acc, fa[pc], fb[pc]);
-                    // the loads of part kk of issue_units_part (both units: LPT in all)
-                    interleave<NMF, DSR, (kk + 1) * C::LPT / KK - kk * C::LPT / KK>();
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-                constexpr int pl = (p0 + KK - 1) & 1;  // set of the last k-step; the next tile's first uses pl^1
-                ml.template issue_units_part<KK - 1, KK, op1, op2>(t1, d1, t2, d2);
-                // ready(t+1) and free(t): the units newer than B(t+1) may stay in flight
-                wait_vmcnt<WAITN>();
-                ml.fixup_ragged_k(t + 1, slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>());
-                if constexpr (CTR) {
-                    wait_lgkmcnt0();  // this wave's reads of tile t have drained
-                    compiler_fence();
-                    constexpr int sr = (u + 1) % D;
-                    count_up(ctr + D + u);                    // tile t's stage free
-                    if constexpr (LOADER) count_up(ctr + sr);  // tile t+1's stage ready (own loads landed)
-                    late |= wait_count(ctr + sr, C::NL * (t0 / D + (u + 1 == D ? 1 : 0) + 1));
-                } else {
-                    ring_barrier();
-                }
-                ml.read_frags(slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
-                ML::mma(acc, fa[pl], fb[pl]);
-                interleave<NMF, DSR, 0>();
+            constexpr int u = UU;
+            const int t = t0 + u;
+            // the two units refilled during tile t
+            constexpr int s1 = 2 * u + U - 2, s2 = 2 * u + U - 1;
+            constexpr int op1 = s1 % 2, op2 = s2 % 2;
+            const int t1 = t + (U - 2 - op1) / 2, t2 = t + (U - 1 - op2) / 2;
+            IGC_LDS char* d1 = slot<C, Ring::slot_of(U, s1)>();
+            IGC_LDS char* d2 = slot<C, Ring::slot_of(U, s2)>();
+            constexpr int p0 = (u * KK) & 1;  // fragment set of this tile's k-step 0
+            if constexpr (CTR && LOADER) {
+                // the refill goes into the stage of tile t-1 (pass (t-1)/D, P == D here): every
+                // wave must be done reading it; nothing to wait for before tile 0
+                constexpr int sf = (u + D - 1) % D;
+                late |= wait_count(ctr + D + sf, C::NW * (t0 / D + (u >= 1 ? 1 : 0)));
+            }
+            // k-steps 0 .. KK-2: refill, read ahead, MFMA
+            static_for<0, KK - 1>([&](auto KI) __attribute__((always_inline)) {
+                constexpr int kk = KI;
+                constexpr int pc = (p0 + kk) & 1, pn = pc ^ 1;
+                ml.template issue_units_part<kk, KK, op1, op2>(t1, d1, t2, d2);
+                ml.read_frags(slot_a<C, u>(), slot_b<C, u>(), kk + 1, fa[pn], fb[pn]);
+                ML::mma(acc, fa[pc], fb[pc]);
+                // the loads of part kk of issue_units_part (both units: LPT in all)
+                interleave<NMF, DSR, (kk + 1) * C::LPT / KK - kk * C::LPT / KK>();
                 __builtin_amdgcn_sched_barrier(0);
+            });
+            constexpr int pl = (p0 + KK - 1) & 1;  // set of the last k-step; the next tile's first uses pl^1
+            ml.template issue_units_part<KK - 1, KK, op1, op2>(t1, d1, t2, d2);
+            // ready(t+1) and free(t): the units newer than B(t+1) may stay in flight
+            wait_vmcnt<WAITN>();
+            ml.fixup_ragged_k(t + 1, slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>());
+            if constexpr (CTR) {
+                wait_lgkmcnt0();  // this wave's reads of tile t have drained
+                compiler_fence();
+                constexpr int sr = (u + 1) % D;
+                count_up(ctr + D + u);                    // tile t's stage free
+                if constexpr (LOADER) count_up(ctr + sr);  // tile t+1's stage ready (own loads landed)
+                late |= wait_count(ctr + sr, C::NL * (t0 / D + (u + 1 == D ? 1 : 0) + 1));
+            } else {
+                ring_barrier();
+            }
+            ml.read_frags(slot_a<C, (u + 1) % P>(), slot_b<C, (u + 1) % P>(), 0, fa[pl ^ 1], fb[pl ^ 1]);
+            ML::mma(acc, fa[pl], fb[pl]);
+            interleave<NMF, DSR, 0>();
+            __builtin_amdgcn_sched_barrier(0);
         };
         // Whole periods in the loop; the tiles of a last, partial period run
         // after it, each under its own test (those past KT are skipped, though
