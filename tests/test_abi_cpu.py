@@ -426,3 +426,43 @@ def test_ring_rejects_bad_args():
         igc.igc_ring_schedule(0, 4)
     with pytest.raises(ValueError):
         igc.igc_ring_schedule(1, 4, 1)
+
+
+GEMM_SHAPES = [(m, n, k) for m in (1, 200, 1000, 2048, 8192, 100352) for n in (8, 64, 96, 256, 1024, 8192)
+               for k in (8, 256, 1024, 4096, 16384, 65536)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("la,lb", [(igc.ROW_MAJOR, igc.ROW_MAJOR), (igc.ROW_MAJOR, igc.COL_MAJOR),
+                                   (igc.COL_MAJOR, igc.ROW_MAJOR), (igc.COL_MAJOR, igc.COL_MAJOR)])
+def test_builtin_gemm_choice_is_built(dtype, la, lb):
+    """For every shape, the built-in schedule of a GEMM names a compiled instance for that input type and
+    operand layout: the call gets past the instance lookup and fails only on the null A pointer (no launch)."""
+    fn = igc.gemm_fp16_ex if dtype == "fp16" else igc.gemm_bf16_ex
+    for (M, N, K) in GEMM_SHAPES:
+        lda = K if la == igc.ROW_MAJOR else M
+        ldb = N if lb == igc.ROW_MAJOR else K
+        st = fn(M, N, K, None, lda, la, FAKE, ldb, lb, FAKE, N, igc.OUT_F32, None, None, 0, stream=0)
+        assert st == igc.IGC_ERR_INVALID_VALUE, (M, N, K, igc.igc_status_string(st))
+
+
+CONV_SHAPES = [
+    # N, H, W, C, K, R, S, sh, pad
+    (32, 56, 56, 256, 256, 3, 3, 1, 1), (32, 56, 56, 256, 512, 3, 3, 2, 1), (32, 56, 56, 256, 64, 1, 1, 1, 0),
+    (32, 28, 28, 96, 192, 3, 3, 1, 1), (16, 27, 27, 256, 256, 3, 3, 1, 1), (1, 7, 7, 8, 8, 3, 3, 1, 1),
+    (64, 14, 14, 512, 512, 3, 3, 1, 1), (8, 112, 112, 64, 64, 7, 7, 2, 3), (2, 300, 300, 16, 24, 5, 5, 1, 2),
+    (4, 9, 9, 1024, 1024, 1, 1, 1, 0), (128, 7, 7, 2048, 512, 1, 1, 1, 0), (1, 33, 17, 40, 40, 3, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("op", ["fprop", "dgrad", "wgrad"])
+def test_builtin_conv_choice_is_built(op, dtype):
+    """The same for the three convolution operations: the built-in schedule is compiled for the operation and
+    input type on every shape, so the call fails only on the null input pointer."""
+    name = {"fprop": "conv2d_nhwc_implicit_gemm", "dgrad": "conv2d_nhwc_dgrad_implicit_gemm",
+            "wgrad": "conv2d_nhwc_wgrad_implicit_gemm"}[op] + ("_fp16" if dtype == "fp16" else "") + "_ex"
+    fn = getattr(igc, name)
+    for (N, H, W, C, K, R, S, sh, pad) in CONV_SHAPES:
+        st = fn(N, H, W, C, K, R, S, sh, sh, pad, pad, 1, 1, None, FAKE, FAKE, igc.OUT_F32, None, None, 0, stream=0)
+        assert st == igc.IGC_ERR_INVALID_VALUE, (op, N, H, W, C, K, R, S, igc.igc_status_string(st))
