@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import implicit_gemm_conv_amd as igc
@@ -466,3 +467,27 @@ def test_builtin_conv_choice_is_built(op, dtype):
     for (N, H, W, C, K, R, S, sh, pad) in CONV_SHAPES:
         st = fn(N, H, W, C, K, R, S, sh, sh, pad, pad, 1, 1, None, FAKE, FAKE, igc.OUT_F32, None, None, 0, stream=0)
         assert st == igc.IGC_ERR_INVALID_VALUE, (op, N, H, W, C, K, R, S, igc.igc_status_string(st))
+
+
+def test_builtin_split_invariants():
+    """Whenever the built-in schedule splits K, the split fills at least 7/8 of the 256 CUs and leaves every part
+    at least 2048 of K (8192 for 256 x 128 tiles outside the filter gradient); the split tiles are the only ones
+    the rule uses (256 x 128 or 128 x 128)."""
+    rng = np.random.default_rng(5)
+    checked = 0
+    for _ in range(3000):
+        M, N = (int(v) for v in rng.integers(1, 3000, 2))
+        K = int(rng.choice([1024, 4096, 8192, 16384, 32768, 65536, 131072]))
+        op = int(rng.choice([igc.OP_GEMM, igc.OP_CONV_FPROP, igc.OP_CONV_DGRAD, igc.OP_CONV_WGRAD]))
+        t = igc.igc_default_tune(M, N, K, op=op)
+        if t.k_splits <= 1:
+            continue
+        checked += 1
+        bm, bn = t.astuple()[:2]
+        assert (bm, bn) in ((256, 128), (128, 128)), (M, N, K, op, t.astuple())
+        tiles = -(-M // bm) * -(-N // bn)
+        assert tiles * t.k_splits * 8 >= 256 * 7 and tiles * t.k_splits <= 256, (M, N, K, op, t.k_splits)
+        kmin = 8192 if (bm, bn) == (256, 128) and op != igc.OP_CONV_WGRAD else 2048
+        assert K // t.k_splits >= kmin, (M, N, K, op, t.k_splits)
+        assert t.stream_k == 0
+    assert checked > 100
