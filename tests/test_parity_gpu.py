@@ -209,6 +209,32 @@ def test_workload_conv_sampled(name, out):
         f"max err/S {max_err_over_s(got, ref, S):.3g}")
 
 
+@pytest.mark.parametrize("name", ["conv_bf16_n32_56x56_c256_k256_3x3", "conv_bf16_n32_56x56_c256_k64_1x1",
+                                  "conv_bf16_n32_28x28_c96_k192_3x3"])
+def test_workload_conv_fp16_sampled(name):
+    """The fp16 forward convolution at the named workloads' full sizes and distributions (fp16 inputs drawn with
+    the same seed, fp16 output) on the built-in tile -- 224-row, 256 x 64 and 128 x 64 tiles here: every output
+    channel of the border pixels of the first and last image and 200k seeded samples."""
+    cfg = inputs.WORKLOADS[name]
+    geo = dict(sh=cfg["sh"], sw=cfg["sw"], ph=cfg["ph"], pw=cfg["pw"], dh=cfg["dh"], dw=cfg["dw"])
+    Nn, H, W, C, K, R, S = (cfg[k] for k in ("N", "H", "W", "C", "K", "R", "S"))
+    x, w = inputs.conv_operands(Nn, H, W, C, K, R, S, "fp16", cfg["a_dist"], cfg["b_dist"], seed=cfg["seed"])
+    P, Q = oracle.conv_out_hw(H, W, R, S, **geo)
+    say(f"workload {name} fp16 -> f16")
+    y, _ = run_conv(Nn, H, W, C, K, R, S, x, w, out="f16", dtype="fp16", **geo)
+    rng = np.random.default_rng(cfg["seed"] + 100)
+    idx = [rng.integers(0, y.size, 200000)]
+    for n in (0, Nn - 1):
+        for p in sorted({0, 1, P - 2, P - 1} & set(range(P))):
+            for q in sorted({0, 1, Q - 2, Q - 1} & set(range(Q))):
+                base = ((n * P + p) * Q + q) * K
+                idx.append(np.arange(base, base + K))
+    idx = np.concatenate(idx).astype(np.int64)
+    ref, Sabs = oracle.conv2d_nhwc_sample(Nn, H, W, C, K, R, S, x, w, oracle.FP16, idx, **geo)
+    r = assert_close(y.ravel()[idx], ref, Sabs, "f16", f"{name} fp16")
+    say(f"  {idx.size} outputs checked, max err/bound {r:.3g}")
+
+
 # ---------------------------------------------------------------------------
 # boundary tiles, ragged K, layouts, types
 # ---------------------------------------------------------------------------
